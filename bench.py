@@ -1,0 +1,254 @@
+#!/usr/bin/env python3
+"""Benchmark of the chunk-wise causal attention layer tick on one MI355X.
+
+One step = one round of the hot path on one layer: wf_kv_publish of the live
+store and the W slot chunks (3D RoPE on K + paged scatter of K and V), then
+wf_chunk_attn of the W query chunks over the pool (anchor | history | store |
+slots j >= s), back to back on one stream.  Inputs are synthetic and resident
+in HBM before the timed region; the resident prefix (anchor + history) is
+published once before timing.
+
+    python bench.py [--steps K] [--warmup W] [--config 4] [--no-cpu-baseline]
+
+Prints one JSON line.  `value` is the unmasked attention TFLOP/s of the
+whole step (publish included in the time); `roofline` describes the
+attention kernel (MFMA-bound), measured with HIP events on the launch
+stream; `cpu_baseline` times the CPU oracle on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
+METRIC = "chunk-causal attn TFLOP/s (unmasked) & % bf16 MFMA peak; layer tick ms"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=4, choices=[2, 3, 4, 5])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only plain device copies of a known size (for counter scaling)")
+    return ap.parse_args()
+
+
+def device_inputs(cfg, torch, wf):
+    """Synthetic inputs of the configuration's shape, drawn on the device
+    (same distributions as chunk_wise_causal_amd.workloads, other values)."""
+    from chunk_wise_causal_amd.workloads import Config  # noqa: F401  (shape source)
+    dev = "cuda"
+    g = torch.Generator(device=dev).manual_seed(1000 + cfg.seed)
+    gc = torch.Generator().manual_seed(1000 + cfg.seed)
+    H, D = cfg.heads, cfg.head_dim
+    td = torch.bfloat16
+    q = torch.randn(cfg.n_q, H, D, device=dev, generator=g).to(td)
+    k = torch.randn(cfg.n_kv, H, D, device=dev, generator=g)
+    n_hot = int(round(cfg.hot_frac * cfg.n_kv))
+    if n_hot:
+        k[torch.randperm(cfg.n_kv, generator=gc)[:n_hot].to(dev)] *= cfg.hot_factor
+    k = k.to(td)
+    v = torch.randn(cfg.n_kv, H, D, device=dev, generator=g).to(td)
+    perm = torch.randperm(cfg.n_pages, generator=gc) if cfg.permute_pages else torch.arange(cfg.n_pages)
+    table = perm[:cfg.n_logical_pages].to(torch.int32)
+    pool = wf.KVPool.empty(cfg.n_pages, H, cfg.page_size, D, table, dtype=td, device=dev)
+    pool.k_pages.normal_(0.0, 2.0, generator=g)     # stale contents
+    pool.v_pages.normal_(0.0, 2.0, generator=g)
+    pos = torch.from_numpy(cfg.positions()).to(dev)
+    return q, k, v, pos, pool
+
+
+def copy_calibration(torch):
+    """Plain copies of exactly 1 GiB each: the bytes a FETCH_SIZE / WRITE_SIZE
+    counter reports for them give the scale from counter units to bytes."""
+    n = 1 << 29                      # 2^29 bf16 = 1 GiB
+    a = torch.empty(n, dtype=torch.bfloat16, device="cuda").normal_()
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": 2 * n, "copy_bytes_written": 2 * n, "copies": 3}))
+
+
+def traffic_from_profiles(kernel_src_hash: str):
+    """HBM bytes per attention launch from the committed counter summary, or
+    None when it is missing or was taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", "attn_fwd_bf16_cfg4_traffic.json")
+    try:
+        with open(path) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("source_sha256") != kernel_src_hash:
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in ("attn_bf16.hip", "wf_internal.h"):
+        with open(os.path.join(ROOT, "chunk_wise_causal_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def cpu_baseline(cfg, seconds: float):
+    """Time the CPU oracle (as it stands) on a bounded sample of the same
+    workload: whole heads of attention (all slots, all rows) until `seconds`
+    have passed, and a publish of 2048 tokens; scale both to a full step."""
+    import torch
+    from chunk_wise_causal_amd.workloads import make_workload
+    import dataclasses
+    from oracle.attention import chunk_attention
+    from oracle.publish import publish
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = 1
+    # a copy of the configuration with at most 8 heads: same layout and pages
+    small = dataclasses.replace(cfg, heads=min(cfg.heads, 8))
+    wl = make_workload(small)
+    from tests._pipeline import oracle_layer  # test glue: oracle-only pipeline
+    t0 = time.perf_counter()
+    ref = oracle_layer(wl)
+    t_pub_all = time.perf_counter() - t0
+    c = wl.cfg
+    done_heads, t_attn = 0, 0.0
+    while done_heads < c.heads and t_attn < seconds:
+        t0 = time.perf_counter()
+        chunk_attention(ref["k_pool"], ref["v_pool"], wl.page_table, c.page_size, c.segments(),
+                        ref["q"], c.q_slot_start(), 0, c.scale, c.dtype, heads=[done_heads])
+        t_attn += time.perf_counter() - t0
+        done_heads += 1
+    flops_per_head = cfg.unmasked_flops() / cfg.heads
+    attn_full = t_attn / done_heads * cfg.heads
+    # publish: the oracle published all n_kv tokens of the copy's heads
+    pub_full = t_pub_all * (cfg.tick_tokens / c.n_kv) * (cfg.heads / c.heads)
+    step = attn_full + pub_full
+    return {
+        "value": cfg.unmasked_flops() / step / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"float64 numpy oracle: attention of {done_heads} head(s) x all "
+                   f"{cfg.slots} slots x {cfg.chunk} rows ({done_heads * flops_per_head:.3e} "
+                   f"unmasked flops, {t_attn:.1f} s) and publish of {c.n_kv} tokens x "
+                   f"{c.heads} heads ({t_pub_all:.1f} s), scaled by flops and bytes to one "
+                   f"full step ({step:.0f} s)"),
+        "step_s_extrapolated": step,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this path has no multi-GPU mode "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
+    from chunk_wise_causal_amd import wf
+    from chunk_wise_causal_amd.workloads import CONFIGS
+    wf.lib()
+    cfg = CONFIGS[args.config]
+    q, k, v, pos, pool = device_inputs(cfg, torch, wf)
+    out = torch.empty_like(q)
+    segs = cfg.segments()
+    qss = cfg.q_slot_start()
+    ss = cfg.store_start
+    rope = (cfg.rope, cfg.theta)
+    # resident prefix (anchor + history), published once before the round
+    wf.wf_kv_publish(pool, k[:ss], v[:ss], 0, pos=pos[:ss], rope=rope)
+    k_t, v_t, pos_t = k[ss:], v[ss:], pos[ss:]
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        wf.wf_kv_publish(pool, k_t, v_t, ss, pos=pos_t, rope=rope, stream=stream)
+        if ev:
+            ev[1].record(stream)
+        wf.wf_chunk_attn(pool, segs, q, qss, 0, cfg.scale, out=out, stream=stream)
+        if ev:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pub_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    attn_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    tick_ms = [e[0].elapsed_time(e[2]) for e in evs]
+    assert wf.wf_device_status() == 0
+    ms_step = wall * 1e3 / args.steps
+    flops = cfg.unmasked_flops()
+    attn_avg = float(np.mean(attn_ms))
+    attn_tflops = flops / (attn_avg * 1e-3) / 1e12
+    pub_bytes = cfg.publish_bytes()
+    pub_avg = float(np.mean(pub_ms))
+    pub_gbps = pub_bytes / (pub_avg * 1e-3) / 1e9
+    res = {
+        "metric": METRIC,
+        "value": round(flops / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: Q/K/V ~ N(0,1) bf16 drawn on device, seeded; random-permuted pages",
+        "config": {"workload": f"layer tick, cfg{args.config}: {cfg.name}",
+                   "heads": cfg.heads, "head_dim": cfg.head_dim, "chunk": cfg.chunk,
+                   "anchor": cfg.anchor_tokens, "history_chunks": cfg.n_hist,
+                   "slots": cfg.slots, "n_q": cfg.n_q, "n_kv": cfg.n_kv,
+                   "page_size": cfg.page_size, "unmasked_flops": flops,
+                   "publish_tokens": cfg.tick_tokens, "publish_bytes": pub_bytes},
+        "tick_ms_p50": round(float(np.median(tick_ms)), 4),
+        "attn_ms_p50": round(float(np.median(attn_ms)), 4),
+        "attn_ms_p10_p90": [round(float(np.percentile(attn_ms, 10)), 4),
+                            round(float(np.percentile(attn_ms, 90)), 4)],
+        "attn_tflops": round(attn_tflops, 2),
+        "publish_ms_p50": round(float(np.median(pub_ms)), 4),
+        "publish_GBps": round(pub_gbps, 1),
+        "publish_frac_hbm_peak": round(pub_gbps / PEAK_HBM_GBPS, 4),
+        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic_from_profiles(kernel_source_hash()),
+                     "kernel": "attn_fwd_bf16<128>"},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,307 @@
+// Host side of libwf: argument validation, the slot-mask schedule, launches.
+//
+// Every check runs before the first HIP call, so a rejected call has no side
+// effect and the checks can be exercised on a machine without a GPU.
+//
+// Source of the method: "Wave Forcing: Towards Speed-of-Light Streaming Video
+// Generation", §3.1 (chunk-wise causal mask and context order) and §4.2
+// (K/V published after QKV projection and RoPE into paged attention slots).
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/wf.h"
+#include "wf_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return WF_OK;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(WF_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int log2_exact(int v) {
+  int l = 0;
+  while ((1 << l) < v) ++l;
+  return ((1 << l) == v) ? l : -1;
+}
+
+int check_pool(const wf_kv_pool* pool) {
+  if (!pool) return fail(WF_ERR_INVALID, "pool is NULL");
+  if (!pool->k_pages || !pool->v_pages || !pool->page_table)
+    return fail(WF_ERR_INVALID, "pool: k_pages, v_pages and page_table must be non-NULL");
+  if (pool->dtype != WF_BF16 && pool->dtype != WF_FP32)
+    return fail(WF_ERR_INVALID, "pool: dtype %d is not WF_BF16 or WF_FP32", pool->dtype);
+  if (pool->num_heads < 1) return fail(WF_ERR_INVALID, "pool: num_heads must be >= 1");
+  if (pool->num_pages < 1 || pool->num_logical_pages < 1)
+    return fail(WF_ERR_INVALID, "pool: num_pages and num_logical_pages must be >= 1");
+  if (pool->page_size < 16 || pool->page_size > 1024 || log2_exact(pool->page_size) < 0)
+    return fail(WF_ERR_INVALID, "pool: page_size %d is not a power of two in [16, 1024]",
+                pool->page_size);
+  if (pool->head_dim != 64 && pool->head_dim != 128)
+    return fail(WF_ERR_UNSUPPORTED, "pool: head_dim %d not supported (64 or 128)",
+                pool->head_dim);
+  if (!aligned16(pool->k_pages) || !aligned16(pool->v_pages))
+    return fail(WF_ERR_INVALID, "pool: page arrays must be 16-byte aligned");
+  const int64_t elems = (int64_t)pool->num_pages * pool->num_heads * pool->page_size *
+                        pool->head_dim;
+  if (elems > (int64_t(1) << 40))
+    return fail(WF_ERR_UNSUPPORTED, "pool: too large");
+  return WF_OK;
+}
+
+int check_rows(const char* name, const void* ptr, int64_t stride, const wf_kv_pool* pool) {
+  if (!ptr) return fail(WF_ERR_INVALID, "%s is NULL", name);
+  if (!aligned16(ptr)) return fail(WF_ERR_INVALID, "%s must be 16-byte aligned", name);
+  const int64_t row = (int64_t)pool->num_heads * pool->head_dim;
+  if (stride < row)
+    return fail(WF_ERR_INVALID, "%s_row_stride %lld < num_heads*head_dim %lld", name,
+                (long long)stride, (long long)row);
+  if (stride % 8 != 0)
+    return fail(WF_ERR_INVALID, "%s_row_stride %lld is not a multiple of 8", name,
+                (long long)stride);
+  return WF_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* wf_last_error(void) { return g_err.c_str(); }
+
+const char* wf_version(void) { return "libwf 0.1.0 gfx950"; }
+
+int wf_device_status(int32_t* status, int32_t clear) {
+  if (!status) return fail(WF_ERR_INVALID, "status is NULL");
+  hipError_t e;
+  int* p = wf::status_word_ptr(&e);
+  if (!p) return hip_fail(e, "status word");
+  int v = 0;
+  if ((e = hipDeviceSynchronize()) != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
+  if ((e = hipMemcpy(&v, p, sizeof v, hipMemcpyDeviceToHost)) != hipSuccess)
+    return hip_fail(e, "read status");
+  if (clear) {
+    const int zero = 0;
+    if ((e = hipMemcpy(p, &zero, sizeof zero, hipMemcpyHostToDevice)) != hipSuccess)
+      return hip_fail(e, "clear status");
+  }
+  *status = v;
+  return ok();
+}
+
+int wf_kv_publish(const wf_kv_pool* pool, const wf_rope* rope, const void* k,
+                  int64_t k_row_stride, const void* v, int64_t v_row_stride,
+                  const int32_t* pos_thw, int32_t n_tok, int32_t dst_logical_start,
+                  void* q_inout, int64_t q_row_stride, hipStream_t stream) {
+  int rc = check_pool(pool);
+  if (rc) return rc;
+  if (n_tok < 0) return fail(WF_ERR_INVALID, "n_tok %d < 0", n_tok);
+  if (dst_logical_start < 0)
+    return fail(WF_ERR_INVALID, "dst_logical_start %d < 0", dst_logical_start);
+  const int64_t cap = (int64_t)pool->num_logical_pages * pool->page_size;
+  if ((int64_t)dst_logical_start + n_tok > cap)
+    return fail(WF_ERR_INVALID, "dst_logical_start + n_tok = %lld exceeds pool capacity %lld",
+                (long long)dst_logical_start + n_tok, (long long)cap);
+  wf::PublishParams p{};
+  if (rope) {
+    if (rope->d_t < 0 || rope->d_h < 0 || rope->d_w < 0 || (rope->d_t & 1) ||
+        (rope->d_h & 1) || (rope->d_w & 1))
+      return fail(WF_ERR_INVALID, "rope: sub-band widths must be even and >= 0");
+    if (rope->d_t + rope->d_h + rope->d_w != pool->head_dim)
+      return fail(WF_ERR_INVALID, "rope: d_t + d_h + d_w = %d != head_dim %d",
+                  rope->d_t + rope->d_h + rope->d_w, pool->head_dim);
+    if (!(rope->theta > 0.0) || !std::isfinite(rope->theta))
+      return fail(WF_ERR_INVALID, "rope: theta must be finite and > 0");
+    if (n_tok > 0 && !pos_thw) return fail(WF_ERR_INVALID, "pos_thw is NULL with rope");
+  }
+  if (q_inout && !rope) return fail(WF_ERR_INVALID, "q_inout requires rope");
+  if (n_tok > 0) {
+    if ((rc = check_rows("k", k, k_row_stride, pool))) return rc;
+    if ((rc = check_rows("v", v, v_row_stride, pool))) return rc;
+    if (q_inout && (rc = check_rows("q", q_inout, q_row_stride, pool))) return rc;
+  }
+  if (n_tok == 0) return ok();
+
+  p.k = k;
+  p.v = v;
+  p.q = q_inout;
+  p.k_pages = pool->k_pages;
+  p.v_pages = pool->v_pages;
+  p.page_table = pool->page_table;
+  p.pos = pos_thw;
+  p.k_stride = k_row_stride;
+  p.v_stride = v_row_stride;
+  p.q_stride = q_inout ? q_row_stride : 0;
+  p.n_tok = n_tok;
+  p.dst_start = dst_logical_start;
+  p.heads = pool->num_heads;
+  p.head_dim = pool->head_dim;
+  p.ps_log2 = log2_exact(pool->page_size);
+  p.num_pages = pool->num_pages;
+  p.num_logical_pages = pool->num_logical_pages;
+  p.rope = rope ? 1 : 0;
+  if (rope) {
+    // frequencies of every pair: theta^(-2i/d_a), evaluated in double
+    const int d[3] = {rope->d_t, rope->d_h, rope->d_w};
+    int pair = 0;
+    for (int a = 0; a < 3; ++a)
+      for (int i = 0; i < d[a] / 2; ++i, ++pair) {
+        p.pair_axis[pair] = a;
+        p.pair_omega[pair] = std::pow(rope->theta, (-2.0 * i) / (double)d[a]);
+      }
+  }
+  // heads per block: enough blocks to fill the chip, as few RoPE factor
+  // evaluations as that allows
+  const int64_t tiles = ((int64_t)dst_logical_start + n_tok - 1) / 64 -
+                        dst_logical_start / 64 + 1;
+  int64_t hpb = (int64_t)pool->num_heads * tiles / 2048;
+  p.heads_per_block = (int)std::max<int64_t>(1, std::min<int64_t>(hpb, pool->num_heads));
+
+  hipError_t e;
+  p.status = wf::status_word_ptr(&e);
+  if (!p.status) return hip_fail(e, "status word");
+  if ((e = wf::launch_publish(p, pool->dtype, stream)) != hipSuccess)
+    return hip_fail(e, "publish launch");
+  return ok();
+}
+
+int wf_chunk_attn(const wf_kv_pool* pool, const wf_segment* segs, int32_t n_segs,
+                  const void* q, int64_t q_row_stride, const int32_t* q_slot_start,
+                  int32_t n_slots, int32_t first_slot, float scale, void* out,
+                  int64_t out_row_stride, float* lse, hipStream_t stream) {
+  int rc = check_pool(pool);
+  if (rc) return rc;
+  if (!segs) return fail(WF_ERR_INVALID, "segs is NULL");
+  if (n_segs < 1 || n_segs > 64) return fail(WF_ERR_INVALID, "n_segs %d not in [1, 64]", n_segs);
+  if (!q_slot_start) return fail(WF_ERR_INVALID, "q_slot_start is NULL");
+  if (n_slots < 1 || n_slots > wf::kMaxGroups)
+    return fail(WF_ERR_INVALID, "n_slots %d not in [1, %d]", n_slots, wf::kMaxGroups);
+  if (first_slot < 0 || first_slot > (1 << 30))
+    return fail(WF_ERR_INVALID, "first_slot %d out of range", first_slot);
+  if (!(scale > 0.f) || !std::isfinite(scale))
+    return fail(WF_ERR_INVALID, "scale must be finite and > 0");
+  const int64_t cap = (int64_t)pool->num_logical_pages * pool->page_size;
+  std::vector<wf_segment> sorted(segs, segs + n_segs);
+  for (int i = 0; i < n_segs; ++i) {
+    const wf_segment& s = segs[i];
+    if (s.kv_len < 1 || s.kv_start < 0 || (int64_t)s.kv_start + s.kv_len > cap)
+      return fail(WF_ERR_INVALID, "segment %d [%d, +%d) outside the pool's %lld tokens", i,
+                  s.kv_start, s.kv_len, (long long)cap);
+  }
+  std::sort(sorted.begin(), sorted.end(),
+            [](const wf_segment& a, const wf_segment& b) { return a.kv_start < b.kv_start; });
+  for (int i = 1; i < n_segs; ++i)
+    if ((int64_t)sorted[i - 1].kv_start + sorted[i - 1].kv_len > sorted[i].kv_start)
+      return fail(WF_ERR_INVALID, "segments overlap at token %d", sorted[i].kv_start);
+  if (q_slot_start[0] < 0) return fail(WF_ERR_INVALID, "q_slot_start[0] < 0");
+  for (int g = 0; g < n_slots; ++g)
+    if (q_slot_start[g + 1] < q_slot_start[g])
+      return fail(WF_ERR_INVALID, "q_slot_start is not non-decreasing at %d", g);
+  for (int g = 0; g < n_slots; ++g) {
+    bool own = false;
+    for (int i = 0; i < n_segs; ++i) own |= (segs[i].slot == first_slot + g);
+    if (!own)
+      return fail(WF_ERR_INVALID, "query slot %d owns no segment", first_slot + g);
+  }
+  const int total_rows = q_slot_start[n_slots];
+  const bool any_rows = total_rows > q_slot_start[0];
+  if (any_rows) {
+    if ((rc = check_rows("q", q, q_row_stride, pool))) return rc;
+    if ((rc = check_rows("out", out, out_row_stride, pool))) return rc;
+  }
+
+  // ---- slot-mask schedule: merged visible ranges per group ([WF] §3.1) ----
+  wf::AttnParams p{};
+  struct G { int g; int64_t vis; };
+  std::vector<G> order;
+  std::vector<std::vector<int2>> granges(n_slots);
+  int n_ranges = 0;
+  for (int g = 0; g < n_slots; ++g) {
+    const int s = first_slot + g;
+    std::vector<int2>& r = granges[g];
+    int64_t vis = 0;
+    for (const wf_segment& sg : sorted) {
+      if (!(sg.slot < 0 || sg.slot >= s)) continue;
+      const int lo = sg.kv_start, hi = sg.kv_start + sg.kv_len;
+      vis += hi - lo;
+      if (!r.empty() && r.back().y == lo) r.back().y = hi;
+      else r.push_back(make_int2(lo, hi));
+    }
+    n_ranges += (int)r.size();
+    order.push_back({g, vis});
+  }
+  if (n_ranges > wf::kMaxRanges)
+    return fail(WF_ERR_UNSUPPORTED, "%d visible ranges exceed the limit of %d", n_ranges,
+                wf::kMaxRanges);
+  if (!any_rows) return ok();
+
+  const bool bf16 = pool->dtype == WF_BF16;
+  const int bm = bf16 ? wf::kBlockMBf16 : wf::kBlockMFp32;
+  // longest visible context first (largest tiles start first), ties by group
+  std::stable_sort(order.begin(), order.end(),
+                   [](const G& a, const G& b) { return a.vis > b.vis; });
+  int nr = 0, tiles = 0, k = 0;
+  for (const G& o : order) {
+    const int rows = q_slot_start[o.g + 1] - q_slot_start[o.g];
+    if (rows == 0) continue;
+    tiles += (rows + bm - 1) / bm;
+    p.grp_tile_end[k] = tiles;
+    p.grp_row0[k] = q_slot_start[o.g];
+    p.grp_row1[k] = q_slot_start[o.g + 1];
+    p.grp_rng0[k] = nr;
+    for (const int2& r : granges[o.g]) p.ranges[nr++] = r;
+    p.grp_rng1[k] = nr;
+    ++k;
+  }
+  p.n_groups = k;
+  p.tiles_per_head = tiles;
+  p.q = q;
+  p.out = out;
+  p.lse = lse;
+  p.k_pages = pool->k_pages;
+  p.v_pages = pool->v_pages;
+  p.page_table = pool->page_table;
+  p.q_stride = q_row_stride;
+  p.out_stride = out_row_stride;
+  p.heads = pool->num_heads;
+  p.ps_log2 = log2_exact(pool->page_size);
+  p.num_pages = pool->num_pages;
+  p.num_logical_pages = pool->num_logical_pages;
+  p.lse_stride = total_rows;
+  p.scale = scale;
+  p.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  const int64_t blocks = (int64_t)tiles * pool->num_heads;
+  if (blocks > 0x7fffffff) return fail(WF_ERR_UNSUPPORTED, "too many query tiles");
+
+  hipError_t e;
+  p.status = wf::status_word_ptr(&e);
+  if (!p.status) return hip_fail(e, "status word");
+  e = bf16 ? wf::launch_attn_bf16(p, pool->head_dim, bm, stream)
+           : wf::launch_attn_fp32(p, pool->head_dim, bm, stream);
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,74 @@
+// Internal launch interface of libwf: kernel parameter blocks shared by the
+// host API (api.cpp) and the kernels (publish.hip, attn_bf16.hip,
+// attn_fp32.hip).  Parameter blocks travel as kernel arguments, so a launch
+// captures everything it needs and concurrent calls never share state.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace wf {
+
+constexpr int kMaxGroups = 32;     // query groups (slots) per attention call
+constexpr int kMaxRanges = 256;    // merged visible ranges over all groups
+constexpr int kMaxPairs = 64;      // head_dim / 2 for head_dim <= 128
+
+// ---- publish ---------------------------------------------------------------
+struct PublishParams {
+  const void* k;        // [n_tok] rows of [H][D]
+  const void* v;
+  void* q;              // nullable, rotated in place
+  void* k_pages;        // [pages][H][ps][D]
+  void* v_pages;        // [pages][H][D][ps]
+  const int32_t* page_table;
+  const int32_t* pos;   // [n_tok][3], nullable when !rope
+  int* status;          // device status word
+  int64_t k_stride, v_stride, q_stride;   // elements between token rows
+  int32_t n_tok, dst_start;
+  int32_t heads, head_dim, ps_log2, num_pages, num_logical_pages;
+  int32_t heads_per_block;
+  int32_t rope;         // 0/1
+  int32_t pair_axis[kMaxPairs];     // axis (0 t, 1 h, 2 w) of each pair
+  double pair_omega[kMaxPairs];     // theta^(-2i/d_a) of each pair
+};
+
+// ---- attention -----------------------------------------------------------
+struct AttnParams {
+  const void* q;
+  void* out;
+  float* lse;           // nullable, [H][lse_stride]
+  const void* k_pages;
+  const void* v_pages;
+  const int32_t* page_table;
+  int* status;
+  int64_t q_stride, out_stride;      // elements between rows
+  int32_t heads, ps_log2, num_pages, num_logical_pages;
+  int32_t lse_stride;                // = q_slot_start[n_slots]
+  float scale;                       // softmax scale
+  float scale_log2;                  // scale * log2(e)
+  int32_t n_groups;
+  int32_t tiles_per_head;            // sum of query tiles of all groups
+  // groups in work order (longest visible context first)
+  int32_t grp_tile_end[kMaxGroups];  // cumulative query tiles, work order
+  int32_t grp_row0[kMaxGroups];      // first query row
+  int32_t grp_row1[kMaxGroups];      // one past the last query row
+  int32_t grp_rng0[kMaxGroups];      // first visible range of the group
+  int32_t grp_rng1[kMaxGroups];      // one past its last visible range
+  int2 ranges[kMaxRanges];           // [lo, hi) logical key ranges, sorted
+};
+
+// launches (stream-ordered; return hipError_t of the launch)
+hipError_t launch_publish(const PublishParams& p, int dtype, hipStream_t stream);
+hipError_t launch_attn_bf16(const AttnParams& p, int head_dim, int block_m,
+                            hipStream_t stream);
+hipError_t launch_attn_fp32(const AttnParams& p, int head_dim, int block_m,
+                            hipStream_t stream);
+
+// per-device status word (status.hip)
+int* status_word_ptr(hipError_t* err);
+
+// query-tile height of each attention kernel
+constexpr int kBlockMBf16 = 128;
+constexpr int kBlockMFp32 = 64;
+
+}  // namespace wf

@@ -1,0 +1,182 @@
+"""ctypes binding of libwf (include/wf.h), argument marshalling only.
+
+Every step of the path runs in the library's HIP kernels; this module turns
+torch tensors into device pointers, Python lists into host arrays and the
+current torch stream into a hipStream_t, and raises WFError on a non-zero
+status.  torch provides device memory and streams, nothing else.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Sequence, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libwf.so")
+
+WF_OK, WF_ERR_INVALID, WF_ERR_UNSUPPORTED, WF_ERR_HIP = 0, -1, -2, -3
+WF_BF16, WF_FP32 = 0, 1
+WF_STATUS_BAD_PAGE = 1
+
+
+class WFError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"libwf error {code}: {msg}")
+        self.code = code
+
+
+class wf_kv_pool(ctypes.Structure):
+    _fields_ = [("k_pages", ctypes.c_void_p), ("v_pages", ctypes.c_void_p),
+                ("page_table", ctypes.c_void_p), ("num_pages", ctypes.c_int32),
+                ("num_logical_pages", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("num_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
+
+
+class wf_rope(ctypes.Structure):
+    _fields_ = [("d_t", ctypes.c_int32), ("d_h", ctypes.c_int32), ("d_w", ctypes.c_int32),
+                ("theta", ctypes.c_double)]
+
+
+class wf_segment(ctypes.Structure):
+    _fields_ = [("kv_start", ctypes.c_int32), ("kv_len", ctypes.c_int32),
+                ("slot", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libwf.so (built in-tree by chunk_wise_causal_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m chunk_wise_causal_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+        L.wf_kv_publish.argtypes = [ctypes.POINTER(wf_kv_pool), ctypes.POINTER(wf_rope),
+                                    vp, i64, vp, i64, vp, i32, i32, vp, i64, vp]
+        L.wf_kv_publish.restype = ctypes.c_int
+        L.wf_chunk_attn.argtypes = [ctypes.POINTER(wf_kv_pool), ctypes.POINTER(wf_segment), i32,
+                                    vp, i64, ctypes.POINTER(i32), i32, i32, ctypes.c_float,
+                                    vp, i64, vp, vp]
+        L.wf_chunk_attn.restype = ctypes.c_int
+        L.wf_last_error.restype = ctypes.c_char_p
+        L.wf_last_error.argtypes = []
+        L.wf_version.restype = ctypes.c_char_p
+        L.wf_version.argtypes = []
+        L.wf_device_status.argtypes = [ctypes.POINTER(i32), i32]
+        L.wf_device_status.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(rc: int):
+    if rc != WF_OK:
+        raise WFError(rc, lib().wf_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _row_stride(t: torch.Tensor, name: str) -> int:
+    if t.dim() != 3 or t.stride(2) != 1 or t.stride(1) != t.shape[2]:
+        raise ValueError(f"{name}: expected [rows, heads, head_dim] with contiguous rows")
+    return t.stride(0)
+
+
+class KVPool:
+    """A paged K/V pool in device memory (layout of include/wf.h):
+    k_pages [num_pages, H, page_size, D], v_pages [num_pages, H, D, page_size]
+    and the page table [num_logical_pages] (int32)."""
+
+    def __init__(self, k_pages: torch.Tensor, v_pages: torch.Tensor, page_table: torch.Tensor):
+        n, H, ps, D = k_pages.shape
+        if tuple(v_pages.shape) != (n, H, D, ps):
+            raise ValueError("v_pages must be [num_pages, H, D, page_size]")
+        if page_table.dtype != torch.int32 or page_table.dim() != 1:
+            raise ValueError("page_table must be a 1-D int32 tensor")
+        if not (k_pages.is_contiguous() and v_pages.is_contiguous() and page_table.is_contiguous()):
+            raise ValueError("pool tensors must be contiguous")
+        self.k_pages, self.v_pages, self.page_table = k_pages, v_pages, page_table
+        self.dtype = {torch.bfloat16: WF_BF16, torch.float32: WF_FP32}[k_pages.dtype]
+        self.desc = wf_kv_pool(k_pages.data_ptr(), v_pages.data_ptr(), page_table.data_ptr(),
+                               n, page_table.numel(), ps, H, D, self.dtype)
+
+    @classmethod
+    def empty(cls, num_pages: int, heads: int, page_size: int, head_dim: int,
+              page_table: torch.Tensor, dtype=torch.bfloat16, device="cuda", fill=None):
+        k = torch.empty(num_pages, heads, page_size, head_dim, dtype=dtype, device=device)
+        v = torch.empty(num_pages, heads, head_dim, page_size, dtype=dtype, device=device)
+        if fill is not None:
+            k.fill_(fill)
+            v.fill_(fill)
+        return cls(k, v, page_table.to(device=device, dtype=torch.int32).contiguous())
+
+    @property
+    def page_size(self) -> int:
+        return self.desc.page_size
+
+
+def wf_kv_publish(pool: KVPool, k: torch.Tensor, v: torch.Tensor, dst_start: int,
+                  pos: Optional[torch.Tensor] = None,
+                  rope: Optional[Tuple[Tuple[int, int, int], float]] = None,
+                  q: Optional[torch.Tensor] = None, stream=None) -> None:
+    """RoPE K (and q, in place) with `pos` and scatter K, V into the pool at
+    logical rows dst_start.. (C: wf_kv_publish)."""
+    n = k.shape[0]
+    r = None
+    if rope is not None:
+        (dt, dh, dw), theta = rope
+        r = wf_rope(dt, dh, dw, float(theta))
+    ks = _row_stride(k, "k")
+    vs = _row_stride(v, "v")
+    qs = _row_stride(q, "q") if q is not None else 0
+    if pos is not None and (pos.dtype != torch.int32 or not pos.is_contiguous()):
+        raise ValueError("pos must be a contiguous int32 [n, 3] tensor")
+    rc = lib().wf_kv_publish(ctypes.byref(pool.desc), ctypes.byref(r) if r else None,
+                             _ptr(k), ks, _ptr(v), vs, _ptr(pos), n, dst_start,
+                             _ptr(q), qs, _stream(stream))
+    _check(rc)
+
+
+def wf_chunk_attn(pool: KVPool, segments: Sequence[Tuple[int, int, int]], q: torch.Tensor,
+                  q_slot_start: Sequence[int], first_slot: int = 0,
+                  scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                  lse: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Chunk-wise causal attention of the query slots over the pool
+    (C: wf_chunk_attn).  Returns `out` ([rows, H, D], allocated if None)."""
+    if out is None:
+        out = torch.empty_like(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    segs = (wf_segment * len(segments))(*[wf_segment(*s) for s in segments])
+    qss = (ctypes.c_int32 * len(q_slot_start))(*q_slot_start)
+    rc = lib().wf_chunk_attn(ctypes.byref(pool.desc), segs, len(segments), _ptr(q),
+                             _row_stride(q, "q"), qss, len(q_slot_start) - 1, first_slot,
+                             float(scale), _ptr(out), _row_stride(out, "out"), _ptr(lse),
+                             _stream(stream))
+    _check(rc)
+    return out
+
+
+def wf_device_status(clear: bool = True) -> int:
+    """OR of WF_STATUS_* bits raised on the current device (synchronizes)."""
+    v = ctypes.c_int32(0)
+    _check(lib().wf_device_status(ctypes.byref(v), 1 if clear else 0))
+    return v.value
+
+
+def version() -> str:
+    return lib().wf_version().decode()

@@ -1,0 +1,92 @@
+"""GPU-side test glue: upload a seeded workload and run it through libwf.
+
+Mirrors tests/_pipeline.py (the oracle side) step for step, so the two pools
+can be compared byte for byte: the same NaN fill, the same stale pages, the
+same two publish calls (resident prefix at set-up, then one round).
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from chunk_wise_causal_amd import wf
+from chunk_wise_causal_amd.workloads import Workload
+
+DEV = "cuda"
+
+
+def gpu_pool(wl: Workload, fill: str = "nan") -> wf.KVPool:
+    c = wl.cfg
+    td = wl.torch_dtype
+    pool = wf.KVPool.empty(c.n_pages, c.heads, c.page_size, c.head_dim,
+                           torch.from_numpy(wl.page_table), dtype=td, device=DEV)
+    for t in (pool.k_pages, pool.v_pages):
+        if fill != "nan":
+            t.zero_()
+        elif td == torch.bfloat16:
+            t.view(torch.int16).fill_(0x7FC1)      # the oracle's quiet-NaN pattern
+        else:
+            t.view(torch.int32).fill_(0x7FC00000)
+    if len(wl.stale_pages):
+        idx = torch.from_numpy(wl.stale_pages).to(DEV)
+        pool.k_pages[idx] = wl.stale_k.to(DEV)
+        pool.v_pages[idx] = wl.stale_v.to(DEV)
+    return pool
+
+
+def gpu_layer(wl: Workload, fill: str = "nan", rope: bool = True, q_inout: bool = False):
+    """Publish set-up and one round with libwf; returns (pool, q, dev)."""
+    c = wl.cfg
+    pool = gpu_pool(wl, fill)
+    k = wl.k.to(DEV)
+    v = wl.v.to(DEV)
+    pos = torch.from_numpy(wl.pos).to(DEV)
+    rp = (c.rope, c.theta) if rope else None
+    ss = c.store_start
+    if ss:
+        wf.wf_kv_publish(pool, k[:ss], v[:ss], 0, pos=pos[:ss] if rope else None, rope=rp)
+    wf.wf_kv_publish(pool, k[ss:], v[ss:], ss, pos=pos[ss:] if rope else None, rope=rp)
+    q = wl.q.to(DEV)
+    return pool, q, dict(k=k, v=v, pos=pos)
+
+
+def attn(wl: Workload, pool: wf.KVPool, q: torch.Tensor, lse: bool = True, **kw):
+    c = wl.cfg
+    args = dict(segments=c.segments(), q_slot_start=c.q_slot_start(), first_slot=0,
+                scale=c.scale)
+    args.update(kw)
+    n_rows = args["q_slot_start"][-1]
+    lse_t = torch.full((c.heads, n_rows), float("nan"), device=DEV) if lse else None
+    out = torch.full_like(q, float("nan"))
+    wf.wf_chunk_attn(pool, args["segments"], q, args["q_slot_start"], args["first_slot"],
+                     args["scale"], out=out, lse=lse_t)
+    torch.cuda.synchronize()
+    return out, lse_t
+
+
+def to_storage(t: torch.Tensor) -> np.ndarray:
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def bits(a: np.ndarray) -> np.ndarray:
+    """Bit patterns of a storage array (so NaNs compare equal to themselves)."""
+    return a.view(np.uint32) if a.dtype == np.float32 else a
+
+
+def to_f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def err_stats(got: np.ndarray, ref: np.ndarray):
+    """(max-abs error, relative RMS error) over all elements."""
+    d = got - ref
+    return float(np.abs(d).max()), float(np.sqrt((d * d).sum() / (ref * ref).sum()))
+
+
+# attention tolerance: max-abs <= 2e-2 and relative RMS <= 5e-3 against the
+# float64 oracle, for bf16 inputs with float32 accumulation
+MAX_ABS = 2e-2
+REL_RMS = 5e-3

@@ -1,0 +1,162 @@
+"""libwf's C ABI on the host (CPU only, no compute calls).
+
+Checks that the library loads, exports every function include/wf.h declares,
+and that every contract violation is rejected with its status code before any
+HIP call: the device pointers passed here are fake addresses that must never
+be dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from chunk_wise_causal_amd import wf
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x7F0000001000          # 16-byte aligned, never touched
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "wf.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(wf_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(wf.LIB_PATH):
+        pytest.skip("libwf.so not built")
+    return wf.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert {"wf_kv_publish", "wf_chunk_attn", "wf_last_error", "wf_device_status",
+            "wf_version"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.wf_version().decode().startswith("libwf")
+
+
+def pool(**kw):
+    d = dict(k_pages=FAKE, v_pages=FAKE + 0x100000, page_table=FAKE + 0x200000,
+             num_pages=10, num_logical_pages=10, page_size=256, num_heads=4, head_dim=128,
+             dtype=wf.WF_BF16)
+    d.update(kw)
+    return wf.wf_kv_pool(**d)
+
+
+def publish(L, p=None, rope=wf.wf_rope(44, 42, 42, 1e4), k=FAKE, ks=512, v=FAKE, vs=512,
+            pos=FAKE, n=100, dst=0, q=None, qs=0):
+    p = p or pool()
+    rc = L.wf_kv_publish(ctypes.byref(p), ctypes.byref(rope) if rope else None, k, ks, v, vs,
+                         pos, n, dst, q, qs, None)
+    return rc, L.wf_last_error().decode()
+
+
+def attn(L, p=None, segs=((0, 100, -1), (100, 50, 0), (150, 50, 1)), q=FAKE, qs=512,
+         qss=(0, 50, 100), first=0, scale=0.088, out=FAKE, os_=512, n_segs=None):
+    p = p or pool()
+    sa = (wf.wf_segment * max(1, len(segs)))(*[wf.wf_segment(*s) for s in segs])
+    qa = (ctypes.c_int32 * len(qss))(*qss)
+    rc = L.wf_chunk_attn(ctypes.byref(p), sa, len(segs) if n_segs is None else n_segs, q, qs,
+                         qa, len(qss) - 1, first, scale, out, os_, None, None)
+    return rc, L.wf_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(page_size=48), wf.WF_ERR_INVALID, "page_size"),
+    (dict(page_size=8), wf.WF_ERR_INVALID, "page_size"),
+    (dict(page_size=2048), wf.WF_ERR_INVALID, "page_size"),
+    (dict(head_dim=96), wf.WF_ERR_UNSUPPORTED, "head_dim"),
+    (dict(head_dim=256), wf.WF_ERR_UNSUPPORTED, "head_dim"),
+    (dict(num_heads=0), wf.WF_ERR_INVALID, "num_heads"),
+    (dict(num_pages=0), wf.WF_ERR_INVALID, "num_pages"),
+    (dict(dtype=7), wf.WF_ERR_INVALID, "dtype"),
+    (dict(k_pages=0), wf.WF_ERR_INVALID, "non-NULL"),
+    (dict(page_table=0), wf.WF_ERR_INVALID, "non-NULL"),
+    (dict(v_pages=FAKE + 8), wf.WF_ERR_INVALID, "aligned"),
+])
+def test_pool_checks_both_calls(L, kw, code, msg):
+    for rc, err in (publish(L, p=pool(**kw)), attn(L, p=pool(**kw))):
+        assert rc == code and msg in err
+
+
+@pytest.mark.parametrize("kw,msg", [
+    (dict(rope=wf.wf_rope(44, 42, 40, 1e4)), "head_dim"),
+    (dict(rope=wf.wf_rope(43, 43, 42, 1e4)), "even"),
+    (dict(rope=wf.wf_rope(44, 42, 42, -1.0)), "theta"),
+    (dict(rope=wf.wf_rope(44, 42, 42, float("inf"))), "theta"),
+    (dict(pos=None), "pos_thw"),
+    (dict(k=None), "k is NULL"),
+    (dict(v=FAKE + 4), "aligned"),
+    (dict(ks=500), "k_row_stride"),
+    (dict(vs=516), "multiple of 8"),
+    (dict(n=-1), "n_tok"),
+    (dict(dst=-5), "dst_logical_start"),
+    (dict(dst=2500, n=61), "capacity"),
+    (dict(rope=None, q=FAKE, qs=512), "q_inout requires rope"),
+    (dict(q=FAKE, qs=256), "q_row_stride"),
+])
+def test_publish_rejects(L, kw, msg):
+    rc, err = publish(L, **kw)
+    assert rc == wf.WF_ERR_INVALID, err
+    assert msg in err
+
+
+def test_publish_zero_tokens_is_noop(L):
+    rc, err = publish(L, n=0, k=None, v=None)
+    assert rc == wf.WF_OK and err == ""
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(segs=((0, 100, -1), (90, 50, 0), (150, 50, 1))), wf.WF_ERR_INVALID, "overlap"),
+    (dict(segs=((0, 100, -1), (100, 50, 0))), wf.WF_ERR_INVALID, "owns no segment"),
+    (dict(segs=((0, 100, -1), (100, 0, 0), (150, 50, 1))), wf.WF_ERR_INVALID, "outside"),
+    (dict(segs=((0, 100, -1), (100, 50, 0), (2550, 50, 1))), wf.WF_ERR_INVALID, "outside"),
+    (dict(segs=((-1, 100, -1), (100, 50, 0), (150, 50, 1))), wf.WF_ERR_INVALID, "outside"),
+    (dict(n_segs=0), wf.WF_ERR_INVALID, "n_segs"),
+    (dict(n_segs=65), wf.WF_ERR_INVALID, "n_segs"),
+    (dict(qss=(0, 60, 50)), wf.WF_ERR_INVALID, "non-decreasing"),
+    (dict(qss=(-2, 50, 100)), wf.WF_ERR_INVALID, "q_slot_start[0]"),
+    (dict(qss=tuple(range(34))), wf.WF_ERR_INVALID, "n_slots"),
+    (dict(first=-1), wf.WF_ERR_INVALID, "first_slot"),
+    (dict(first=1), wf.WF_ERR_INVALID, "owns no segment"),
+    (dict(scale=0.0), wf.WF_ERR_INVALID, "scale"),
+    (dict(scale=float("nan")), wf.WF_ERR_INVALID, "scale"),
+    (dict(q=None), wf.WF_ERR_INVALID, "q is NULL"),
+    (dict(out=FAKE + 2), wf.WF_ERR_INVALID, "aligned"),
+    (dict(os_=256), wf.WF_ERR_INVALID, "out_row_stride"),
+])
+def test_attn_rejects(L, kw, code, msg):
+    rc, err = attn(L, **kw)
+    assert rc == code, err
+    assert msg in err
+
+
+def test_attn_too_many_ranges_unsupported(L):
+    # 32 query slots, each with its own segment, plus 32 prefix segments with
+    # gaps: every slot sees >= 32 unmergeable ranges -> > 256 in total
+    segs = [(i * 20, 10, -1) for i in range(32)] + [(1000 + i * 20, 10, i) for i in range(32)]
+    rc, err = attn(L, segs=segs, qss=tuple(range(0, 330, 10)))
+    assert rc == wf.WF_ERR_UNSUPPORTED and "ranges" in err
+
+
+def test_attn_no_rows_is_noop(L):
+    rc, err = attn(L, qss=(7, 7, 7), q=None, out=None)
+    assert rc == wf.WF_OK and err == ""
+
+
+def test_device_status_null_arg(L):
+    assert L.wf_device_status(None, 0) == wf.WF_ERR_INVALID
+
+
+def test_binding_raises_with_message(L):
+    p = wf.KVPool.__new__(wf.KVPool)
+    p.desc = pool(page_size=100)
+    import torch
+    t = torch.empty(0)
+    with pytest.raises(wf.WFError, match="page_size"):
+        wf.wf_chunk_attn(p, [(0, 10, 0)], torch.empty(4, 4, 128), [0, 4], out=torch.empty(4, 4, 128),
+                         stream=0)
