@@ -38,6 +38,8 @@ namespace wf {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int BM = 128;     // query rows per block
@@ -89,6 +91,24 @@ __device__ __forceinline__ void load_tile(const AttnParams& p, int head, int kt,
   const bool one_page = p.ps_log2 >= 6;           // tile inside one page
   const int tile_page = one_page ? lookup_page(p, max(kt, lo)) : -1;
   const uint4 zero = make_uint4(0, 0, 0, 0);
+  if (one_page && tile_page >= 0 && lo == kt && hi == kt + BN) {
+    // the common case: a whole tile of one page, no masking, no branches
+    const int64_t base = (int64_t)tile_page * p.heads + head;
+    const uint16_t* kb = kpg + (base * ps + (kt & (ps - 1))) * D;
+    const uint16_t* vb = vpg + base * D * ps + (kt & (ps - 1));
+#pragma unroll
+    for (int i = 0; i < Stage<D>::KCH; ++i) {
+      const int c = tid + NT * i;
+      st.k[i] = *reinterpret_cast<const uint4*>(kb + (c / (D / 8)) * D + (c % (D / 8)) * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < Stage<D>::VCH; ++i) {
+      const int c = tid + NT * i;
+      st.v[i] = *reinterpret_cast<const uint4*>(vb + (int64_t)(c / (BN / 8)) * ps +
+                                                (c % (BN / 8)) * 8);
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < Stage<D>::KCH; ++i) {
     const int c = tid + NT * i;
@@ -191,7 +211,9 @@ void attn_fwd_bf16(const AttnParams p) {
 #pragma unroll
   for (int i = 0; i < DB; ++i) o[i] = f32x16{};
   float m_run = -INFINITY;   // running max of scale*log2(e)*<q,k>
-  float l_run = 0.f;         // this half-lane's partial denominator
+  float l_part[PK];          // this half-lane's partial denominators
+#pragma unroll
+  for (int t = 0; t < PK; ++t) l_part[t] = 0.f;
   const float sl2 = p.scale_log2;
 
   // ---- tile cursor over the merged visible ranges -------------------------
@@ -253,20 +275,28 @@ void attn_fwd_bf16(const AttnParams p) {
     if (__builtin_amdgcn_ballot_w64(mt > m_run + kRescaleSlack) != 0) {
       const float m_new = fmaxf(m_run, mt);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= alpha;
+#pragma unroll
+      for (int t = 0; t < PK; ++t) l_part[t] *= alpha;
 #pragma unroll
       for (int i = 0; i < DB; ++i) o[i] *= alpha;
       m_run = m_new;
     }
+    // probabilities, rounded to bf16 for the PV product; the denominator sums
+    // the same rounded values exactly in float, so the weights applied to V
+    // are normalized exactly even when one key dominates a row
     bf16x8 pb[PK];
 #pragma unroll
     for (int t = 0; t < PK; ++t) {
+      uint32_t pk[4];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float pe = __builtin_amdgcn_exp2f(s[t >> 1][8 * (t & 1) + e] * sl2 - m_run);
-        l_run += pe;
-        pb[t][e] = (__bf16)pe;
+      for (int j = 0; j < 4; ++j) {
+        const f32x2 x = {__builtin_amdgcn_exp2f(s[t >> 1][8 * (t & 1) + 2 * j] * sl2 - m_run),
+                         __builtin_amdgcn_exp2f(s[t >> 1][8 * (t & 1) + 2 * j + 1] * sl2 - m_run)};
+        const bf16x2 b = __builtin_convertvector(x, bf16x2);
+        pk[j] = __builtin_bit_cast(uint32_t, b);
+        l_part[t] += __uint_as_float(pk[j] << 16) + __uint_as_float(pk[j] & 0xffff0000u);
       }
+      pb[t] = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
     }
 #pragma unroll
     for (int t = 0; t < PK; ++t) {
@@ -289,6 +319,9 @@ void attn_fwd_bf16(const AttnParams p) {
   }
 
   // ---- epilogue: O = O^T / l, LSE ------------------------------------------
+  float l_run = 0.f;
+#pragma unroll
+  for (int t = 0; t < PK; ++t) l_run += l_part[t];
   const float l = xhalf_sum(l_run);
   const float inv = 1.0f / l;
   if (qvalid) {

@@ -70,4 +70,4 @@ def test_full_size_config(idx):
     print(f"[full] cfg{idx} max-abs {mx:.3e} rel-rms {rr:.3e}", flush=True)
     assert mx <= G.MAX_ABS and rr <= G.REL_RMS
     np.testing.assert_allclose(G.to_f64(lse)[heads][:, sel], l_ref[heads][:, sel],
-                               rtol=0, atol=1e-3)
+                               rtol=0, atol=G.lse_atol(cfg.dtype))

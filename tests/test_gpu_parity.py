@@ -2,7 +2,7 @@
 
 publish: bit-exact, byte for byte over the whole pool (written rows, NaN
 fill, stale pages).  attention: max-abs <= 2e-2 and relative RMS <= 5e-3
-against the float64 oracle; LSE within 1e-3.  Shapes span several query and
+against the float64 oracle; LSE within the derived bound (2.5e-3 bf16).  Shapes span several query and
 key tiles, ragged query tails, unaligned slot boundaries, every page-size
 regime (smaller than, equal to and larger than a 64-key tile), head_dim 64
 and 128, bf16 and fp32.
@@ -77,7 +77,7 @@ def test_attention_matches_oracle(case):
     mx, rr = G.err_stats(got, o_ref)
     print(f"max-abs {mx:.3e} rel-rms {rr:.3e}", flush=True)
     assert mx <= G.MAX_ABS and rr <= G.REL_RMS
-    np.testing.assert_allclose(G.to_f64(lse), l_ref, rtol=0, atol=1e-3)
+    np.testing.assert_allclose(G.to_f64(lse), l_ref, rtol=0, atol=G.lse_atol(c.dtype))
     assert wf.wf_device_status() == 0
 
 
