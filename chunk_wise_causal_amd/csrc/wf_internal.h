@@ -68,7 +68,7 @@ hipError_t launch_attn_fp32(const AttnParams& p, int head_dim, int block_m,
 int* status_word_ptr(hipError_t* err);
 
 // query-tile height of each attention kernel
-constexpr int kBlockMBf16 = 128;
+constexpr int kBlockMBf16 = 256;
 constexpr int kBlockMFp32 = 64;
 
 }  // namespace wf

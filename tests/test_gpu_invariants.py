@@ -117,3 +117,25 @@ def test_deterministic():
     o1, l1 = G.attn(wl, pool, q)
     o2, l2 = G.attn(wl, pool, q)
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("ps", [64, 256])
+def test_repeatable_across_calls_and_grid_shapes(ps):
+    """The same rows computed by differently shaped launches (all slots in
+    one call, one slot per call) and by repeated calls agree bit for bit.
+    A write-after-read race between waves on an LDS slot shows up here as a
+    run-to-run or launch-to-launch difference."""
+    wl = make_workload(cfg(page_size=ps, stale_frac=0.0, seed=43))
+    c = wl.cfg
+    pool, q, _ = G.gpu_layer(wl)
+    ref, ref_lse = G.attn(wl, pool, q)
+    qs = c.q_slot_start()
+    for rep in range(4):
+        out, lse = G.attn(wl, pool, q)
+        assert torch.equal(out, ref) and torch.equal(lse, ref_lse), rep
+        for s in range(c.slots):
+            r0, r1 = qs[s], qs[s + 1]
+            part, lse_p = G.attn(wl, pool, q[r0:r1].contiguous(), q_slot_start=[0, r1 - r0],
+                                 first_slot=s)
+            assert torch.equal(part, ref[r0:r1]), (rep, s)
+            assert torch.equal(lse_p, ref_lse[:, r0:r1]), (rep, s)
