@@ -172,12 +172,15 @@ int wf_kv_publish(const wf_kv_pool* pool, const wf_rope* rope, const void* k,
         p.pair_omega[pair] = std::pow(rope->theta, (-2.0 * i) / (double)d[a]);
       }
   }
-  // heads per block: enough blocks to fill the chip, as few RoPE factor
-  // evaluations as that allows
-  const int64_t tiles = ((int64_t)dst_logical_start + n_tok - 1) / 64 -
-                        dst_logical_start / 64 + 1;
-  int64_t hpb = (int64_t)pool->num_heads * tiles / 2048;
-  p.heads_per_block = (int)std::max<int64_t>(1, std::min<int64_t>(hpb, pool->num_heads));
+  // 64-token tiles of the window; K blocks take up to 8 heads (the rotary
+  // factors of a tile are evaluated once per K block), V blocks one head
+  const int64_t tiles = ((int64_t)dst_logical_start + n_tok - 1) / 64 - dst_logical_start / 64 + 1;
+  p.tiles = (int)tiles;
+  p.heads_per_kblock = std::min(pool->num_heads, 8);
+  const int64_t kgroups = (pool->num_heads + p.heads_per_kblock - 1) / p.heads_per_kblock;
+  const int64_t blocks = tiles * kgroups + tiles * pool->num_heads;
+  if (blocks > 0x7fffffff) return fail(WF_ERR_UNSUPPORTED, "publish window too large");
+  p.k_blocks = (int)(tiles * kgroups);
 
   hipError_t e;
   p.status = wf::status_word_ptr(&e);

@@ -5,15 +5,22 @@
 // K/V are published after the QKV projection and RoPE, straight into ordered
 // paged attention slots, with no concatenation step.
 //
-// One block owns a 64-token tile of logical rows (aligned to 64 in logical
-// space) and a group of heads.  It first evaluates the rotary factors of its
-// tokens once (double-precision angle and cos/sin, rounded to float) into
-// LDS, then for every head of its group:
-//   K: 16-byte vector load -> rotate pairs in float (no fused multiply-add)
-//      -> round to the storage type -> 16-byte store into the K page row;
-//   V: rows staged in LDS, re-read by feature d, and stored as runs of 8
-//      consecutive tokens into the d-major V page (16-byte stores for bf16).
-// Memory-bound: every byte of K and V is read once and written once.
+// Memory-bound: every byte of K and V is read once and written once.  One
+// launch runs two kinds of blocks, each shaped for what it moves:
+//   K blocks  (64-token tile x a group of heads, in two passes of 32 tokens):
+//             evaluate the rotary factors of the pass's tokens once
+//             (double-precision angle and cos/sin, rounded to float) into
+//             LDS, then for every head of the group
+//             16-byte vector load -> rotate pairs in float (no fused
+//             multiply-add) -> round to the storage type -> 16-byte store
+//             into the K page row.  Registers are kept low (one head in
+//             flight per thread) so that six blocks share a CU.
+//   V blocks  (64-token tile x one head): rows staged in LDS, re-read by
+//             feature d and stored as runs of 8 consecutive tokens into the
+//             d-major V page (16-byte stores for bf16).  Thousands of small
+//             blocks keep enough bytes in flight.
+// Token tiles are aligned to 64 in logical space, so an 8-token run never
+// crosses a page (pages hold >= 16 tokens).
 #include <type_traits>
 
 #include "../../include/wf.h"
@@ -48,31 +55,56 @@ __device__ __forceinline__ void rotate(float x0, float x1, float2 cs, float& y0,
   y1 = c + d;
 }
 
-template <int D, bool BF16>
-__global__ __launch_bounds__(kThreads) void publish_kernel(const PublishParams p) {
-  using T = typename std::conditional<BF16, uint16_t, float>::type;
-  constexpr int EPV = 16 / sizeof(T);        // elements per 16-byte vector
-  constexpr int VPR = D / EPV;               // vectors per head row
-  constexpr int VPAD = BF16 ? 8 : 4;         // LDS row padding (elements)
-  __shared__ float2 cs[kTileTok][D / 2];
-  __shared__ __attribute__((aligned(16))) T vt[kTileTok][D + VPAD];
-  __shared__ int page_of[kTileTok];
+// rotate the pairs of one 16-byte vector in place (storage type T)
+template <typename T>
+__device__ __forceinline__ void rotate_vec(uint4& v, const float2* cs) {
+  constexpr int EPV = 16 / sizeof(T);
+  T* e = reinterpret_cast<T*>(&v);
+#pragma unroll
+  for (int j = 0; j < EPV / 2; ++j) {
+    float y0, y1;
+    if constexpr (sizeof(T) == 2) {
+      rotate(bf16_to_f32(e[2 * j]), bf16_to_f32(e[2 * j + 1]), cs[j], y0, y1);
+      e[2 * j] = f32_to_bf16_rne(y0);
+      e[2 * j + 1] = f32_to_bf16_rne(y1);
+    } else {
+      rotate(e[2 * j], e[2 * j + 1], cs[j], y0, y1);
+      e[2 * j] = y0;
+      e[2 * j + 1] = y1;
+    }
+  }
+}
 
+// Streaming 16-byte loads and stores: every input byte is read once and every
+// pool byte written once, so neither is kept for reuse (nontemporal).
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 ld_stream(const void* ptr) {
+  return __builtin_bit_cast(uint4, __builtin_nontemporal_load(static_cast<const u32x4*>(ptr)));
+}
+
+__device__ __forceinline__ void st_stream(void* ptr, uint4 v) {
+  __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), static_cast<u32x4*>(ptr));
+}
+
+template <int D, typename T>
+union PublishShared {
+  static constexpr int VPAD = 16 / sizeof(T);   // LDS row padding (elements)
+  float2 cs[kTileTok / 2][D / 2];               // K blocks: rotary factors (32 tokens)
+  T vt[kTileTok][D + VPAD];                     // V blocks: staged rows
+};
+
+// physical page of every token of the tile (-1: outside the published window
+// or a bad page-table entry, which also raises the status bit)
+__device__ __forceinline__ void tile_pages(const PublishParams& p, int L0, int lo, int hi,
+                                           int* page_of) {
   const int tid = threadIdx.x;
-  const int ps = 1 << p.ps_log2;
-  const int L0 = (p.dst_start / kTileTok + (int)blockIdx.x) * kTileTok;
-  const int lo = max(L0, p.dst_start);
-  const int hi = min(L0 + kTileTok, p.dst_start + p.n_tok);
-  const int h0 = (int)blockIdx.y * p.heads_per_block;
-  const int h1 = min(p.heads, h0 + p.heads_per_block);
-
   if (tid < kTileTok) {
     const int L = L0 + tid;
-    const int lp = L >> p.ps_log2;
     int page = -1;
-    // host validation keeps lp < num_logical_pages for published rows
+    // host validation keeps L >> ps_log2 < num_logical_pages for published rows
     if (L >= lo && L < hi) {
-      page = p.page_table[lp];
+      page = p.page_table[L >> p.ps_log2];
       if (page < 0 || page >= p.num_pages) {
         atomicOr(p.status, WF_STATUS_BAD_PAGE);
         page = -1;
@@ -80,124 +112,183 @@ __global__ __launch_bounds__(kThreads) void publish_kernel(const PublishParams p
     }
     page_of[tid] = page;
   }
-  if (p.rope) {
-    for (int idx = tid; idx < kTileTok * (D / 2); idx += kThreads) {
-      const int ti = idx / (D / 2), pr = idx % (D / 2);
-      const int L = L0 + ti;
-      if (L < lo || L >= hi) continue;
-      const int t = L - p.dst_start;
-      const double phi = (double)p.pos[(int64_t)t * 3 + p.pair_axis[pr]] * p.pair_omega[pr];
-      double s, c;
-      sincos(phi, &s, &c);
-      cs[ti][pr] = make_float2((float)c, (float)s);
-    }
-  }
-  __syncthreads();
+}
 
+template <int D, bool BF16, bool HAS_Q>
+__device__ __forceinline__ void k_block(
+    const PublishParams& p, int b,
+    PublishShared<D, typename std::conditional<BF16, uint16_t, float>::type>& sm,
+    int* page_of) {
+  using T = typename std::conditional<BF16, uint16_t, float>::type;
+  constexpr int EPV = 16 / sizeof(T);        // elements per 16-byte vector
+  constexpr int VPR = D / EPV;               // vectors per head row
+  constexpr int HALF = kTileTok / 2;         // tokens per factor pass
+  constexpr int PER = HALF * VPR / kThreads; // vectors per thread per head and pass
+  const int tid = threadIdx.x;
+  const int ps = 1 << p.ps_log2;
+  const int tile = b % p.tiles, grp = b / p.tiles;
+  const int L0 = (p.dst_start / kTileTok + tile) * kTileTok;
+  const int lo = max(L0, p.dst_start);
+  const int hi = min(L0 + kTileTok, p.dst_start + p.n_tok);
+  const int h0 = grp * p.heads_per_kblock;
+  const int h1 = min(p.heads, h0 + p.heads_per_kblock);
   const T* __restrict__ kin = static_cast<const T*>(p.k);
-  const T* __restrict__ vin = static_cast<const T*>(p.v);
   T* qio = static_cast<T*>(p.q);
   T* __restrict__ kpg = static_cast<T*>(p.k_pages);
-  T* __restrict__ vpg = static_cast<T*>(p.v_pages);
 
-  for (int h = h0; h < h1; ++h) {
-    // ---- K (and Q): rotate and store rows --------------------------------
-    for (int idx = tid; idx < kTileTok * VPR; idx += kThreads) {
-      const int ti = idx / VPR, c = idx % VPR;
-      const int L = L0 + ti;
-      if (L < lo || L >= hi) continue;
-      const int64_t t = L - p.dst_start;
-      uint4 kv = *reinterpret_cast<const uint4*>(kin + t * p.k_stride + h * D + c * EPV);
-      if (p.rope) {
-        T* e = reinterpret_cast<T*>(&kv);
-        uint4 qv;
-        T* qe = reinterpret_cast<T*>(&qv);
-        T* qptr = qio ? qio + t * p.q_stride + h * D + c * EPV : nullptr;
-        if (qptr) qv = *reinterpret_cast<const uint4*>(qptr);
+  tile_pages(p, L0, lo, hi, page_of);
+  // two passes of 32 tokens keep the factor table at half the LDS of the
+  // staged V rows, so K and V blocks reach the same occupancy
+  for (int half = 0; half < 2; ++half) {
+    const int T0 = L0 + half * HALF;
+    if (half) __syncthreads();   // every thread is done with the previous factors
+    if (p.rope) {
+      for (int idx = tid; idx < HALF * (D / 2); idx += kThreads) {
+        const int ti = idx / (D / 2), pr = idx % (D / 2);
+        const int L = T0 + ti;
+        if (L < lo || L >= hi) continue;
+        const int t = L - p.dst_start;
+        const double phi = (double)p.pos[(int64_t)t * 3 + p.pair_axis[pr]] * p.pair_omega[pr];
+        double sn, cn;
+        sincos(phi, &sn, &cn);
+        sm.cs[ti][pr] = make_float2((float)cn, (float)sn);
+      }
+    }
+    __syncthreads();   // factors (and, in the first pass, page_of) visible
+    // vectors of this thread: idx = tid + kThreads * i -> (token ti, vector c);
+    // source and destination bases are fixed for the pass, each head adds a
+    // uniform offset (h*D in the rows, h*ps*D in the pages)
+    const T* src[PER];
+    T* qptr[PER];
+    T* dst[PER];
+    int fidx[PER];
 #pragma unroll
-        for (int j = 0; j < EPV / 2; ++j) {
-          const float2 f = cs[ti][c * (EPV / 2) + j];
-          float y0, y1;
-          if constexpr (BF16) {
-            rotate(bf16_to_f32(e[2 * j]), bf16_to_f32(e[2 * j + 1]), f, y0, y1);
-            e[2 * j] = f32_to_bf16_rne(y0);
-            e[2 * j + 1] = f32_to_bf16_rne(y1);
-            if (qptr) {
-              rotate(bf16_to_f32(qe[2 * j]), bf16_to_f32(qe[2 * j + 1]), f, y0, y1);
-              qe[2 * j] = f32_to_bf16_rne(y0);
-              qe[2 * j + 1] = f32_to_bf16_rne(y1);
-            }
-          } else {
-            rotate(e[2 * j], e[2 * j + 1], f, y0, y1);
-            e[2 * j] = y0;
-            e[2 * j + 1] = y1;
-            if (qptr) {
-              rotate(qe[2 * j], qe[2 * j + 1], f, y0, y1);
-              qe[2 * j] = y0;
-              qe[2 * j + 1] = y1;
-            }
+    for (int i = 0; i < PER; ++i) {
+      const int idx = tid + kThreads * i;
+      const int ti = idx / VPR, c = idx % VPR;
+      const int L = T0 + ti;
+      const int64_t t = L - p.dst_start;
+      const bool in = L >= lo && L < hi;
+      const int page = in ? page_of[half * HALF + ti] : -1;
+      src[i] = in ? kin + t * p.k_stride + c * EPV : nullptr;
+      qptr[i] = (in && HAS_Q) ? qio + t * p.q_stride + c * EPV : nullptr;
+      dst[i] = page >= 0 ? kpg + ((int64_t)page * p.heads * ps + (L & (ps - 1))) * D + c * EPV
+                         : nullptr;
+      fidx[i] = ti * (D / 2) + c * (EPV / 2);
+    }
+    const float2* cs = &sm.cs[0][0];
+    for (int h = h0; h < h1; ++h) {
+      uint4 kv[PER], qv[HAS_Q ? PER : 1];
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        if (!src[i]) continue;
+        kv[i] = ld_stream(src[i] + (int64_t)h * D);
+        if constexpr (HAS_Q) qv[i] = *reinterpret_cast<const uint4*>(qptr[i] + (int64_t)h * D);
+      }
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        if (!src[i]) continue;
+        if (p.rope) {
+          rotate_vec<T>(kv[i], cs + fidx[i]);
+          if constexpr (HAS_Q) {
+            rotate_vec<T>(qv[i], cs + fidx[i]);
+            *reinterpret_cast<uint4*>(qptr[i] + (int64_t)h * D) = qv[i];
           }
         }
-        if (qptr) *reinterpret_cast<uint4*>(qptr) = qv;
-      }
-      const int page = page_of[ti];
-      if (page >= 0) {
-        T* dst = kpg + (((int64_t)page * p.heads + h) * ps + (L & (ps - 1))) * D + c * EPV;
-        *reinterpret_cast<uint4*>(dst) = kv;
+        if (dst[i]) st_stream(dst[i] + (int64_t)h * ps * D, kv[i]);
       }
     }
-    // ---- V: stage rows, store d-major runs of 8 tokens ------------------
-    for (int idx = tid; idx < kTileTok * VPR; idx += kThreads) {
-      const int ti = idx / VPR, c = idx % VPR;
-      const int L = L0 + ti;
-      if (L < lo || L >= hi) continue;
-      const int64_t t = L - p.dst_start;
-      *reinterpret_cast<uint4*>(&vt[ti][c * EPV]) =
-          *reinterpret_cast<const uint4*>(vin + t * p.v_stride + h * D + c * EPV);
-    }
-    __syncthreads();
-    for (int idx = tid; idx < D * (kTileTok / 8); idx += kThreads) {
-      const int d = idx / (kTileTok / 8), r8 = idx % (kTileTok / 8);
-      const int ti0 = r8 * 8;
-      const int L = L0 + ti0;
-      if (L + 8 <= lo || L >= hi) continue;
-      // 8-row runs never cross a page (page_size >= 16, runs 8-aligned)
-      int page = -1;
+  }
+}
+
+template <int D, bool BF16>
+__device__ __forceinline__ void v_block(
+    const PublishParams& p, int b,
+    PublishShared<D, typename std::conditional<BF16, uint16_t, float>::type>& sm,
+    int* page_of) {
+  using T = typename std::conditional<BF16, uint16_t, float>::type;
+  constexpr int EPV = 16 / sizeof(T);
+  constexpr int VPR = D / EPV;
+  constexpr int PER = kTileTok * VPR / kThreads;        // staged vectors per thread
+  constexpr int RUNS = D * (kTileTok / 8) / kThreads;   // 8-token runs per thread
+  const int tid = threadIdx.x;
+  const int ps = 1 << p.ps_log2;
+  const int tile = b % p.tiles, h = b / p.tiles;
+  const int L0 = (p.dst_start / kTileTok + tile) * kTileTok;
+  const int lo = max(L0, p.dst_start);
+  const int hi = min(L0 + kTileTok, p.dst_start + p.n_tok);
+  const T* __restrict__ vin = static_cast<const T*>(p.v);
+  T* __restrict__ vpg = static_cast<T*>(p.v_pages);
+
+  tile_pages(p, L0, lo, hi, page_of);
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int idx = tid + kThreads * i;
+    const int ti = idx / VPR, c = idx % VPR;
+    const int L = L0 + ti;
+    if (L < lo || L >= hi) continue;
+    const int64_t t = L - p.dst_start;
+    *reinterpret_cast<uint4*>(&sm.vt[ti][c * EPV]) =
+        ld_stream(vin + t * p.v_stride + (int64_t)h * D + c * EPV);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < RUNS; ++i) {
+    const int idx = tid + kThreads * i;
+    const int d = idx / (kTileTok / 8), r8 = idx % (kTileTok / 8);
+    const int ti0 = r8 * 8;
+    const int L = L0 + ti0;
+    if (L + 8 <= lo || L >= hi) continue;
+    int page = -1;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (L + e >= lo && L + e < hi) page = page_of[ti0 + e];
+    if (page < 0) continue;
+    T* dst = vpg + (((int64_t)page * p.heads + h) * D + d) * ps + (L & (ps - 1));
+    T run[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) run[e] = sm.vt[ti0 + e][d];
+    if (L >= lo && L + 8 <= hi) {
+#pragma unroll
+      for (int v = 0; v < 8 / EPV; ++v)
+        st_stream(reinterpret_cast<uint4*>(dst) + v, reinterpret_cast<const uint4*>(run)[v]);
+    } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        if (L + e >= lo && L + e < hi) page = page_of[ti0 + e];
-      if (page < 0) continue;
-      T* dst = vpg + (((int64_t)page * p.heads + h) * D + d) * ps + (L & (ps - 1));
-      T run[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) run[e] = vt[ti0 + e][d];
-      if (L >= lo && L + 8 <= hi) {
-#pragma unroll
-        for (int v = 0; v < 8 / EPV; ++v)
-          reinterpret_cast<uint4*>(dst)[v] = reinterpret_cast<const uint4*>(run)[v];
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (L + e >= lo && L + e < hi) dst[e] = run[e];
-      }
+        if (L + e >= lo && L + e < hi) dst[e] = run[e];
     }
-    __syncthreads();
   }
+}
+
+template <int D, bool BF16, bool HAS_Q>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(5)))
+void publish_kernel(const PublishParams p) {
+  using T = typename std::conditional<BF16, uint16_t, float>::type;
+  __shared__ __attribute__((aligned(16))) PublishShared<D, T> sm;
+  __shared__ int page_of[kTileTok];
+  const int b = blockIdx.x;
+  if (b < p.k_blocks) k_block<D, BF16, HAS_Q>(p, b, sm, page_of);
+  else v_block<D, BF16>(p, b - p.k_blocks, sm, page_of);
+}
+
+template <int D, bool BF16>
+void launch_typed(const PublishParams& p, dim3 grid, dim3 block, hipStream_t stream) {
+  if (p.q) hipLaunchKernelGGL((publish_kernel<D, BF16, true>), grid, block, 0, stream, p);
+  else hipLaunchKernelGGL((publish_kernel<D, BF16, false>), grid, block, 0, stream, p);
 }
 
 }  // namespace
 
 hipError_t launch_publish(const PublishParams& p, int dtype, hipStream_t stream) {
-  const int tiles = (p.dst_start + p.n_tok - 1) / kTileTok - p.dst_start / kTileTok + 1;
-  dim3 grid(tiles, (p.heads + p.heads_per_block - 1) / p.heads_per_block);
-  dim3 block(kThreads);
+  const int v_blocks = p.tiles * p.heads;
+  dim3 grid(p.k_blocks + v_blocks), block(kThreads);
   const bool bf16 = dtype == WF_BF16;
   if (p.head_dim == 128) {
-    if (bf16) hipLaunchKernelGGL((publish_kernel<128, true>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((publish_kernel<128, false>), grid, block, 0, stream, p);
+    if (bf16) launch_typed<128, true>(p, grid, block, stream);
+    else launch_typed<128, false>(p, grid, block, stream);
   } else {
-    if (bf16) hipLaunchKernelGGL((publish_kernel<64, true>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((publish_kernel<64, false>), grid, block, 0, stream, p);
+    if (bf16) launch_typed<64, true>(p, grid, block, stream);
+    else launch_typed<64, false>(p, grid, block, stream);
   }
   return hipGetLastError();
 }

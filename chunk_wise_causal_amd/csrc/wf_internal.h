@@ -26,7 +26,9 @@ struct PublishParams {
   int64_t k_stride, v_stride, q_stride;   // elements between token rows
   int32_t n_tok, dst_start;
   int32_t heads, head_dim, ps_log2, num_pages, num_logical_pages;
-  int32_t heads_per_block;
+  int32_t tiles;            // 64-token tiles covering the published window
+  int32_t heads_per_kblock;  // heads per K block (rotary factors shared)
+  int32_t k_blocks;         // K blocks; V blocks (tiles * heads) follow
   int32_t rope;         // 0/1
   int32_t pair_axis[kMaxPairs];     // axis (0 t, 1 h, 2 w) of each pair
   double pair_omega[kMaxPairs];     // theta^(-2i/d_a) of each pair
