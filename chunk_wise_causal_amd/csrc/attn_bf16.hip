@@ -18,11 +18,14 @@
 //                 so row max / row sum need a single cross-half exchange.
 //   mask          only on tiles cut by a range boundary: keys outside the
 //                 range become -inf; their K/V rows are never read from HBM
-//                 (zero-filled in LDS), so stale or NaN memory cannot leak.
+//                 (filled in LDS: K with NaN, which the row max skips, V with
+//                 zeros), so stale or NaN memory cannot leak.
 //   softmax       online, base 2, with the running max raised only when a
 //                 row's tile max exceeds it by more than 2^8 (the exact
 //                 result is unchanged: numerator and denominator share the
-//                 stale max, and 2^8 keeps every term finite).  The
+//                 stale max, and 2^8 keeps every term finite).  The max of
+//                 tile j+1 is taken while O += P(j) V(j) runs, so the
+//                 probabilities of a tile never wait for a reduction.  The
 //                 denominator sums the bf16-rounded probabilities that
 //                 multiply V (v_dot2 against 1.0), so the weights applied to
 //                 V are normalized exactly.
@@ -32,12 +35,14 @@
 //                 swapped) so that each lane's 8 probabilities of a k-step
 //                 are 8 consecutive keys, matching a 16-byte V^T read.
 //
-// Pipeline: K runs one tile ahead of V in two LDS double buffers.  While the
-// softmax of tile j runs on the VALU, the MFMAs of S(j+1) = K(j+1) Q^T are
-// already issued; the direct global->LDS loads (global_load_lds_dwordx4) of
-// K(j+2) and V(j+1) are in flight during both.  One barrier per tile.  Tiles
-// cut by a range boundary, spread over several pages or naming a bad page
-// take a register path that zero-fills what lies outside the window.
+// Pipeline: a ring of four LDS slots each for K and V, filled by direct
+// global->LDS loads (global_load_lds_dwordx4) four and two tiles ahead.  Per
+// tile, S(j+1) = K(j+1) Q^T is issued while the softmax of tile j runs, and
+// the max of S(j+1) is taken while O += P(j) V(j) runs.  Half of the waves
+// run half a tile behind the other half (one of each on every SIMD), so the
+// vector work of one overlaps the matrix work of the other.  One barrier per
+// tile.  Tiles cut by a range boundary, spread over several pages or naming
+// a bad page take a register path that fills what lies outside the window.
 //
 // LDS layout: 16-byte chunks XOR-swizzled by row so that the A-operand reads
 // of 8 (or 16) consecutive lanes hit distinct banks: K chunk c of row r sits
@@ -61,7 +66,6 @@ constexpr int NW = 8;       // waves per block, 32 query rows each
 constexpr int BM = 32 * NW; // query rows per block
 constexpr int BN = 64;      // keys per tile
 constexpr int NT = 64 * NW; // threads per block
-constexpr int kStages = 4;  // LDS ring slots for K and for V
 constexpr float kRescaleSlack = 8.0f;   // log2 units
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -113,183 +117,215 @@ __device__ __forceinline__ int table_entry(const AttnParams& p, int logical_page
   return ((const_table_ptr)p.page_table)[logical_page];
 }
 
-// Position of the tile walk over the merged visible ranges of one group.
-// The bounds of the current range and the physical page of the tile are
-// kept with it, so advancing is arithmetic plus one scalar read, issued a
-// step before the tile is loaded.
-struct Cursor {
+// Position of the tile walk over the merged visible ranges of one group:
+// the tile's first key kt, its range [rlo, rhi) and the physical page of
+// the tile (pages of >= BN keys), read a step before the tile is loaded.
+struct Walk {
   int ri;     // current range; == rng1 once past the last tile
-  int kt;     // first key of the tile (multiple of BN)
-  int rlo;    // range [rlo, rhi)
+  int kt;
+  int rlo;
   int rhi;
-  int page;   // physical page of the tile when pages hold >= BN keys
+  int page;
 };
 
-__device__ __forceinline__ void cursor_page(const AttnParams& p, Cursor& c) {
-  if (p.ps_log2 >= 6) c.page = table_entry(p, c.kt >> p.ps_log2);
+// One key tile as the loads and the mask see it, in three scalar registers:
+// ktc = first key | 1 when the tile is cut by its range (ktc < 0: past the
+// end of the walk), ri = its range, page = its physical page (-1 when the
+// tile spans several pages or its page entry is bad).
+struct Tile {
+  int ktc;
+  int ri;
+  int page;
+};
+
+__device__ __forceinline__ void walk_page(const AttnParams& p, Walk& w) {
+  if (p.ps_log2 >= 6) w.page = table_entry(p, w.kt >> p.ps_log2);
 }
 
-__device__ __forceinline__ Cursor cursor_first(const AttnParams& p, int rng0) {
+__device__ __forceinline__ Walk walk_first(const AttnParams& p, int rng0) {
   const int2 r = p.ranges[rng0];
-  Cursor c{rng0, r.x & ~(BN - 1), r.x, r.y, -1};
-  cursor_page(p, c);
-  return c;
+  Walk w{rng0, r.x & ~(BN - 1), r.x, r.y, -1};
+  walk_page(p, w);
+  return w;
 }
 
-__device__ __forceinline__ Cursor cursor_next(const AttnParams& p, int rng1, Cursor c) {
-  c.kt += BN;
-  if (c.kt >= c.rhi) {
-    ++c.ri;
-    if (c.ri >= rng1) return c;
-    const int2 r = p.ranges[c.ri];
-    c.rlo = r.x;
-    c.rhi = r.y;
-    c.kt = r.x & ~(BN - 1);
+__device__ __forceinline__ void walk_next(const AttnParams& p, int rng1, Walk& w) {
+  w.kt += BN;
+  if (w.kt >= w.rhi) {
+    if (++w.ri >= rng1) return;
+    const int2 r = p.ranges[w.ri];
+    w.rlo = r.x;
+    w.rhi = r.y;
+    w.kt = r.x & ~(BN - 1);
   }
-  cursor_page(p, c);
-  return c;
+  walk_page(p, w);
 }
 
-// keys [lo, hi) of the tile at cursor c that lie in its range
-__device__ __forceinline__ void cursor_window(const AttnParams& p, Cursor c, int& lo, int& hi) {
-  lo = max(c.kt, c.rlo);
-  hi = min(c.kt + BN, c.rhi);
+// The tile at the walk position; its page entry is checked here, once.
+__device__ __forceinline__ Tile walk_tile(const AttnParams& p, int rng1, const Walk& w,
+                                          int& bad) {
+  if (w.ri >= rng1) return Tile{-1, 0, -1};
+  const int page = p.ps_log2 >= 6 ? check_page(p, w.page, bad) : -1;
+  const int cut = (w.kt < w.rlo || w.kt + BN > w.rhi) ? 1 : 0;
+  return Tile{w.kt | cut, w.ri, page};
 }
 
-// A wave-uniform pointer, placed in scalar registers (so that a load of
-// base + per-lane 32-bit offset uses the scalar-base addressing form)
-__device__ __forceinline__ const char* uniform_ptr(const char* ptr) {
-  const uint64_t v = reinterpret_cast<uint64_t>(ptr);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-  return reinterpret_cast<const char*>(((uint64_t)hi << 32) | lo);
+__device__ __forceinline__ int tile_kt(const Tile& t) { return t.ktc & ~(BN - 1); }
+__device__ __forceinline__ bool tile_cut(const Tile& t) { return t.ktc & 1; }
+
+// visible keys [lo, hi) of a tile
+__device__ __forceinline__ void tile_window(const AttnParams& p, const Tile& t, int& lo,
+                                            int& hi) {
+  const int2 r = p.ranges[t.ri];
+  lo = max(tile_kt(t), r.x);
+  hi = min(tile_kt(t) + BN, r.y);
 }
+
+// every key of the tile visible and on one good page: the direct-load path
+__device__ __forceinline__ bool tile_full(const Tile& t) { return t.page >= 0 && !tile_cut(t); }
+
+// Block-constant addressing of the loads.  The K page [H][ps][D] and the
+// V page [H][D][ps] of one head have the same size, so one page stride and
+// one per-head offset serve both.
+template <int D>
+struct LoadCtx {
+  static constexpr int PER_K = BN * (D / 8) / NT;   // 16-byte chunks per thread
+  static constexpr int PER_V = D * (BN / 8) / NT;
+  const char* k_head;       // K pages + head offset (bytes)
+  const char* v_head;
+  int64_t page_bytes;
+  uint32_t koff[PER_K];     // per-lane byte offsets of this thread's chunks
+  uint32_t voff[PER_V];
+  uint32_t wave_lds;        // LDS byte address of this wave's first chunk
+};
 
 // Direct global->LDS load, 16 bytes per lane (global_load_lds_dwordx4, the
-// scalar-base form): lane i writes LDS bytes [lds_dst + 16 i, +16).  Issued
-// as inline assembly so that the compiler does not model it: with this
-// LDS-DMA form in the loop its wait bookkeeping drains every later LDS read
-// with lgkmcnt(0), which serializes the A-operand fragment reads.  The
-// caller's explicit vmcnt waits track completion.  The wait states cover a
-// base just written by v_readfirstlane (VALU write of an SGPR read by a
-// memory instruction) and the M0 write read by the LDS-DMA load.
-__device__ __forceinline__ void dma16(const char* sbase, uint32_t voff, void* lds_dst) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds_dst);
+// scalar-base form): lane i writes LDS bytes [M0 + 16 i, +16) with
+// M0 = wave_lds + OFF.  Issued as inline assembly so that the compiler does
+// not model it: with this LDS-DMA form in the loop its wait bookkeeping
+// drains every later LDS read with lgkmcnt(0), which serializes the
+// A-operand fragment reads.  The caller's explicit vmcnt waits track
+// completion.  The wait states cover an SGPR base written by a VALU
+// instruction just before (a memory instruction reading it needs 5) and the
+// M0 write read by the LDS-DMA load (1).
+template <uint32_t OFF>
+__device__ __forceinline__ void dma16(const char* sbase, uint32_t voff, uint32_t wave_lds) {
   asm volatile(
       "s_nop 4\n\t"
-      "s_mov_b32 m0, %2\n\t"
+      "s_add_u32 m0, %2, %3\n\t"
       "s_nop 0\n\t"
       "global_load_lds_dwordx4 %0, %1"
       :
-      : "v"(voff), "s"(sbase), "s"(m0)
-      : "memory", "m0");
+      : "v"(voff), "s"(sbase), "s"(wave_lds), "i"(OFF)
+      : "memory", "m0", "scc");
 }
 
-// ---- global -> LDS: the K tile [BN][D] of one head ------------------------
-// Returns the number of direct global->LDS loads this thread issued, or 0
-// when the register path ran (it waits for every older load as well).
-template <int D>
-__device__ __forceinline__ int load_k(const AttnParams& p, int head, Cursor c,
-                                      uint16_t* __restrict__ kbuf, int& bad) {
-  constexpr int CPR = D / 8;               // chunks per K row
-  constexpr int PER = BN * CPR / NT;       // chunks per thread
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// The PER chunks of one thread: chunk i goes to this wave's 1 KB run i*NW
+// runs further on.
+template <uint32_t SLOT, int I, int PER>
+__device__ __forceinline__ void dma_chunks(const char* base, const uint32_t* off,
+                                           uint32_t wave_lds) {
+  if constexpr (I < PER) {
+    dma16<SLOT + I * NW * 1024>(base, off[I], wave_lds);
+    dma_chunks<SLOT, I + 1, PER>(base, off, wave_lds);
+  }
+}
+
+// ---- global -> LDS: the K tile [BN][D] of one head -------------------------
+// A full tile goes by direct loads (PER_K per thread, left in flight).  Any
+// other tile takes the register path, and a tile past the end of the walk
+// loads nothing; both end with every older vector load complete, so a step
+// never has more than its own direct loads outstanding.
+template <int D, uint32_t SLOT>
+__device__ __forceinline__ void load_k(const AttnParams& p, const LoadCtx<D>& lc, int head,
+                                       const Tile& t, uint16_t* __restrict__ lds, int& bad) {
+  constexpr int CPR = D / 8;   // chunks per K row
+  constexpr int PER = LoadCtx<D>::PER_K;
   const int ps = 1 << p.ps_log2;
-  int lo, hi;
-  cursor_window(p, c, lo, hi);
-  const int kt = c.kt;
-  const uint16_t* __restrict__ kpg = static_cast<const uint16_t*>(p.k_pages);
-  const bool one_page = p.ps_log2 >= 6;    // a 64-aligned tile lies in one page
-  const int tile_page = one_page ? check_page(p, c.page, bad) : -1;
-  if (one_page && tile_page >= 0 && lo == kt && hi == kt + BN) {
-    // chunk i of this thread is row r0 + i*NT/CPR (a multiple of 16 rows
-    // further, so the same swizzled column): one lane offset serves every
-    // chunk, and the per-chunk step goes into the uniform (scalar) base
-    const char* kb = reinterpret_cast<const char*>(
-        kpg + (((int64_t)tile_page * p.heads + head) * ps + (kt & (ps - 1))) * D);
-    const int q = wave * 64 + lane;
-    const int r0 = q / CPR, col = (q % CPR) ^ kswz<D>(r0);
-    const uint32_t loff = (uint32_t)(r0 * D + col * 8) * 2u;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const char* base = uniform_ptr(kb + i * (NT / CPR) * D * 2);
-      dma16(base, loff, kbuf + (i * NW + wave) * 64 * 8);
-    }
-    return PER;
+  if (tile_full(t)) {
+    const char* base = lc.k_head + (int64_t)t.page * lc.page_bytes +
+                       (int64_t)(tile_kt(t) & (ps - 1)) * (D * 2);
+    dma_chunks<SLOT, 0, PER>(base, lc.koff, lc.wave_lds);
+    return;
   }
-  // rare (tile cut by a range boundary, or pages smaller than a tile): one
-  // chunk at a time, to keep register pressure off the hot loop
-  const uint4 zero = make_uint4(0, 0, 0, 0);
+  if (t.ktc >= 0) {
+    // rare (tile cut by a range boundary, spread over several pages, or on a
+    // bad page): one chunk at a time, to keep register pressure off the hot
+    // loop.  Rows outside the window hold bf16 quiet NaNs: their scores are
+    // NaN, which the row max skips (IEEE maxNum), and the mask sets them to
+    // -inf before any exponential, so the max of a cut tile is exact.
+    const int tid = threadIdx.x;
+    const uint16_t* __restrict__ kpg = static_cast<const uint16_t*>(p.k_pages);
+    uint16_t* kbuf = lds + SLOT / 2;
+    const uint4 nan8 = make_uint4(0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u);
+    const uint4 zero = make_uint4(0, 0, 0, 0);
+    const bool one_page = p.ps_log2 >= 6;
+    int lo, hi;
+    tile_window(p, t, lo, hi);
 #pragma unroll 1
-  for (int i = 0; i < PER; ++i) {
-    const int q = (i * NW + wave) * 64 + lane;
-    const int r = q / CPR, col = (q % CPR) ^ kswz<D>(r);
-    const int L = kt + r;
-    uint4 val = zero;
-    if (L >= lo && L < hi) {
-      const int page = one_page ? tile_page : lookup_page(p, L, bad);
-      if (page >= 0)
-        val = *reinterpret_cast<const uint4*>(
-            kpg + (((int64_t)page * p.heads + head) * ps + (L & (ps - 1))) * D + col * 8);
+    for (int i = 0; i < PER; ++i) {
+      const int q = i * NT + tid;
+      const int r = q / CPR, col = (q % CPR) ^ kswz<D>(r);
+      const int L = tile_kt(t) + r;
+      uint4 val = nan8;
+      if (L >= lo && L < hi) {
+        const int page = one_page ? t.page : lookup_page(p, L, bad);
+        val = zero;
+        if (page >= 0)
+          val = *reinterpret_cast<const uint4*>(
+              kpg + (((int64_t)page * p.heads + head) * ps + (L & (ps - 1))) * D + col * 8);
+      }
+      *reinterpret_cast<uint4*>(kbuf + q * 8) = val;
     }
-    *reinterpret_cast<uint4*>(kbuf + q * 8) = val;
   }
-  return 0;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 // ---- global -> LDS: the V^T tile [D][BN] of one head -----------------------
-template <int D>
-__device__ __forceinline__ int load_v(const AttnParams& p, int head, Cursor c,
-                                      uint16_t* __restrict__ vbuf, int& bad) {
-  constexpr int PER = D * (BN / 8) / NT;   // chunks per thread
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// Same contract as load_k.
+template <int D, uint32_t SLOT>
+__device__ __forceinline__ void load_v(const AttnParams& p, const LoadCtx<D>& lc, int head,
+                                       const Tile& t, uint16_t* __restrict__ lds, int& bad) {
+  constexpr int PER = LoadCtx<D>::PER_V;
   const int ps = 1 << p.ps_log2;
-  int lo, hi;
-  cursor_window(p, c, lo, hi);
-  const int kt = c.kt;
-  const uint16_t* __restrict__ vpg = static_cast<const uint16_t*>(p.v_pages);
-  const bool one_page = p.ps_log2 >= 6;
-  const int tile_page = one_page ? check_page(p, c.page, bad) : -1;
-  if (one_page && tile_page >= 0 && lo == kt && hi == kt + BN) {
-    // chunk i of this thread is feature row d0 + i*NT/8 (same swizzle):
-    // one lane offset, the per-chunk step in the uniform base
-    const char* vb = reinterpret_cast<const char*>(
-        vpg + ((int64_t)tile_page * p.heads + head) * D * ps + (kt & (ps - 1)));
-    const int q = wave * 64 + lane;
-    const int d0 = q >> 3, col = (q & 7) ^ vswz(d0);
-    const uint32_t loff = (uint32_t)(d0 * ps + col * 8) * 2u;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const char* base = uniform_ptr(vb + (int64_t)i * (NT / 8) * ps * 2);
-      dma16(base, loff, vbuf + (i * NW + wave) * 64 * 8);
-    }
-    return PER;
+  if (tile_full(t)) {
+    const char* base =
+        lc.v_head + (int64_t)t.page * lc.page_bytes + (int64_t)(tile_kt(t) & (ps - 1)) * 2;
+    dma_chunks<SLOT, 0, PER>(base, lc.voff, lc.wave_lds);
+    return;
   }
-  const uint4 zero = make_uint4(0, 0, 0, 0);
+  if (t.ktc >= 0) {
+    const int tid = threadIdx.x;
+    const uint16_t* __restrict__ vpg = static_cast<const uint16_t*>(p.v_pages);
+    uint16_t* vbuf = lds + SLOT / 2;
+    const uint4 zero = make_uint4(0, 0, 0, 0);
+    const bool one_page = p.ps_log2 >= 6;
+    int lo, hi;
+    tile_window(p, t, lo, hi);
 #pragma unroll 1
-  for (int i = 0; i < PER; ++i) {
-    const int q = (i * NW + wave) * 64 + lane;
-    const int d = q >> 3, col = (q & 7) ^ vswz(d);
-    const int L = kt + col * 8;              // first of the chunk's 8 keys
-    uint4 val = zero;
-    if (L + 8 > lo && L < hi) {
-      // an 8-key run never crosses a page (page_size >= 16, runs 8-aligned)
-      const int page = one_page ? tile_page : lookup_page(p, max(L, lo), bad);
-      if (page >= 0) {
-        val = *reinterpret_cast<const uint4*>(
-            vpg + (((int64_t)page * p.heads + head) * D + d) * ps + (L & (ps - 1)));
-        if (L < lo || L + 8 > hi) {
-          uint16_t* e = reinterpret_cast<uint16_t*>(&val);
+    for (int i = 0; i < PER; ++i) {
+      const int q = i * NT + tid;
+      const int d = q >> 3, col = (q & 7) ^ vswz(d);
+      const int L = tile_kt(t) + col * 8;   // first of the chunk's 8 keys
+      uint4 val = zero;
+      if (L + 8 > lo && L < hi) {
+        // an 8-key run never crosses a page (page_size >= 16, runs 8-aligned)
+        const int page = one_page ? t.page : lookup_page(p, max(L, lo), bad);
+        if (page >= 0) {
+          val = *reinterpret_cast<const uint4*>(
+              vpg + (((int64_t)page * p.heads + head) * D + d) * ps + (L & (ps - 1)));
+          if (L < lo || L + 8 > hi) {
+            uint16_t* e = reinterpret_cast<uint16_t*>(&val);
 #pragma unroll
-          for (int j = 0; j < 8; ++j)
-            if (L + j < lo || L + j >= hi) e[j] = 0;
+            for (int j = 0; j < 8; ++j)
+              if (L + j < lo || L + j >= hi) e[j] = 0;
+          }
         }
       }
+      *reinterpret_cast<uint4*>(vbuf + q * 8) = val;
     }
-    *reinterpret_cast<uint4*>(vbuf + q * 8) = val;
   }
-  return 0;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 template <int D>
@@ -313,6 +349,18 @@ __device__ __forceinline__ void qk(const uint16_t* __restrict__ kbuf, const int*
       s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[i], s[sb], 0, 0, 0);
     }
   }
+}
+
+// Row max of a score tile in log2 units, scaled by sl2 (both halves of the
+// row combined).
+template <int D>
+__device__ __forceinline__ float tile_max(const f32x16* s, float sl2) {
+  float mx = -INFINITY;
+#pragma unroll
+  for (int sb = 0; sb < Frag<D>::SB; ++sb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sb][r]);
+  return xhalf_max(mx) * sl2;
 }
 
 // bf16 probabilities of one tile for running max m, and their sum (over the
@@ -351,6 +399,23 @@ __device__ __forceinline__ void pv(const uint16_t* __restrict__ vbuf, const int*
     }
 }
 
+// Scheduling hint for the block of O += P(j) V(j) and the max of S(j+1):
+// V^T fragment reads run a few products ahead and each MFMA is followed by
+// one vector instruction of the max.
+template <int D>
+__device__ __forceinline__ void interleave_pv_max() {
+  constexpr int NM = Frag<D>::PK * Frag<D>::DB;   // MFMAs of the product
+  constexpr int AHEAD = 3;
+#pragma unroll
+  for (int k = 0; k < AHEAD; ++k) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+  for (int k = 0; k < NM; ++k) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);
+    if (k + AHEAD < NM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+}
+
 // Instruction-scheduling hint for the block that issues the S(j+1) MFMAs and
 // the softmax of tile j: K reads run a few ahead, and every MFMA is followed
 // by a share of the VALU work, so the matrix pipe and the VALU run together.
@@ -358,7 +423,7 @@ template <int D>
 __device__ __forceinline__ void interleave_qk_softmax() {
   constexpr int NM = Frag<D>::SB * Frag<D>::DK;   // MFMAs of S(j+1)
   constexpr int AHEAD = 3;
-  constexpr int VPM = 7;                           // VALU per MFMA
+  constexpr int VPM = 6;                           // VALU per MFMA
 #pragma unroll
   for (int k = 0; k < AHEAD; ++k) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
 #pragma unroll
@@ -386,174 +451,190 @@ __device__ __forceinline__ void mask_tile(f32x16* s, int kt, int w_lo, int w_hi,
     }
 }
 
-// One tile: S(j+1) = K(j+1) Q^T is issued while the softmax of S(j) runs,
-// then O += V(j)^T P(j)^T.  The running max is raised (wave-uniformly) only
-// when some row's tile max exceeds it by more than the slack; that decision
-// is a select, so the probabilities are computed in the same straight-line
-// block as the S(j+1) MFMAs, and only the rare rescale of O and l branches.
+// First half of tile j: S(j+1) = K(j+1) Q^T is issued while the softmax of
+// S(j) runs, producing the bf16 probabilities pb of tile j.  The running max
+// already bounds tile j (it was raised, if needed, while the previous tile's
+// product ran), so the probabilities are at most 2^kRescaleSlack and need no
+// max of their own: one straight-line block of MFMAs and vector work.
 template <int D>
-__device__ __forceinline__ void compute_tile(const uint16_t* __restrict__ kb_next,
-                                             const uint16_t* __restrict__ vb_cur,
-                                             const int* kaddr, const int* vaddr,
-                                             const bf16x8* qf, f32x16* s_cur, f32x16* s_nxt,
-                                             f32x16* o, float& m_run, float* l_acc,
-                                             float sl2) {
-  constexpr int SB = Frag<D>::SB, PK = Frag<D>::PK, DB = Frag<D>::DB;
+__device__ __forceinline__ void softmax_qk(const uint16_t* __restrict__ kb_next, const int* kaddr,
+                                           const bf16x8* qf, const f32x16* s_cur, f32x16* s_nxt,
+                                           float m_run, float* l_acc, float sl2, bf16x8* pb) {
   qk<D>(kb_next, kaddr, qf, s_nxt);
-  float mx = -INFINITY;
-#pragma unroll
-  for (int sb = 0; sb < SB; ++sb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s_cur[sb][r]);
-  const float mt = xhalf_max(mx) * sl2;
-  const bool raise = __builtin_amdgcn_ballot_w64(mt > m_run + kRescaleSlack) != 0;
-  const float m_new = raise ? fmaxf(m_run, mt) : m_run;
-  bf16x8 pb[PK];
   float lsum[2];
-  probs<D>(s_cur, sl2, m_new, pb, lsum);
-  // pin the probabilities above the rescale branch: without a use here the
-  // compiler sinks them below it, out of the block of the S(j+1) MFMAs
+  probs<D>(s_cur, sl2, m_run, pb, lsum);
 #pragma unroll
-  for (int t = 0; t < PK; ++t) asm volatile("" ::"v"(pb[t]));
+  for (int t = 0; t < Frag<D>::PK; ++t) asm volatile("" ::"v"(pb[t]));
   asm volatile("" ::"v"(lsum[0]), "v"(lsum[1]));
   interleave_qk_softmax<D>();
-  if (raise) {
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    l_acc[0] *= alpha;
-    l_acc[1] *= alpha;
-#pragma unroll
-    for (int i = 0; i < DB; ++i) o[i] *= alpha;
-    m_run = m_new;
-  }
   l_acc[0] += lsum[0];
   l_acc[1] += lsum[1];
-  pv<D>(vb_cur, vaddr, pb, o);
 }
 
-// s_waitcnt vmcnt(n) for a wave-uniform n; values beyond the table wait for
-// more than needed, which is always safe
-__device__ __forceinline__ void wait_vmcnt(int n) {
-  if (n >= 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-  else if (n >= 6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
-  else if (n >= 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-  else if (n >= 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
-  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+// Second half of tile j: O += P(j) V(j) while the max of S(j+1) is taken.
+// The running max is raised (wave-uniformly) only when some row's max
+// exceeds it by more than the slack; the caller then rescales O and l.
+template <int D>
+__device__ __forceinline__ bool pv_max(const uint16_t* __restrict__ vbuf, const int* vaddr,
+                                       const bf16x8* pb, f32x16* o, const f32x16* s_nxt,
+                                       float m_run, float sl2, float& m_new) {
+  pv<D>(vbuf, vaddr, pb, o);
+  const float mt = tile_max<D>(s_nxt, sl2);
+  interleave_pv_max<D>();
+  m_new = fmaxf(m_run, mt);
+  return __builtin_amdgcn_ballot_w64(mt > m_run + kRescaleSlack) != 0;
 }
 
-// Ring of NS LDS slots for K and NS for V.  At tile j the slots hold
-// K(j+1..j+NS) and V(j..j+NS-1); step j issues K(j+NS) into the slot of K(j)
-// and V(j+NS-1) into the slot of V(j-1), both read by every wave before the
-// previous barrier, so each load has NS-1 steps to land.  The end of step j
-// needs only K(j+2) and V(j+1), issued NS-2 steps earlier: it waits until
-// no more than the direct loads issued since then are outstanding (vector
-// loads complete in order), then one barrier publishes them to all waves.
-template <int D, int NS>
+// Raise the running max to m_new: O and l scale by 2^(m_run - m_new).
+template <int D>
+__device__ __forceinline__ void rescale(f32x16* o, float* l_acc, float& m_run, float m_new) {
+  const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+  l_acc[0] *= alpha;
+  l_acc[1] *= alpha;
+#pragma unroll
+  for (int i = 0; i < Frag<D>::DB; ++i) o[i] *= alpha;
+  m_run = m_new;
+}
+
+// Ring of NS = 4 LDS slots for K and 4 for V, and two wave groups half a
+// tile apart.  Per tile j every wave runs [S(j+1) + softmax(j)] then
+// [O += P(j) V(j) + max of S(j+1)]; waves 0..NW/2-1 ("leading") take the
+// step's barrier after the second half, waves NW/2.. ("lagging") before it,
+// carrying P(j) in registers across the barrier.  Between two barriers a
+// leading wave thus runs softmax(j) then P(j) V(j) while a lagging wave runs
+// P(j-1) V(j-1) then softmax(j); the two waves sharing a SIMD are one of
+// each group, so while one issues the softmax's vector work the other keeps
+// the matrix pipe busy.
+// At tile j the slots hold K(j+1..j+4) and V(j-1..j+2); step j issues
+// K(j+4) into the slot of K(j) and V(j+2) into the slot of V(j-2), both read
+// by every wave before the previous barrier.  The barrier of step j must
+// publish K(j+2) and V(j+1), issued in earlier steps: each wave waits until
+// no more than this step's direct loads are outstanding (vector loads
+// complete in order), then the barrier publishes them to all waves.
+// The walk runs once per step, four tiles ahead (for K); the tiles in
+// between are kept in a four-entry ring in scalar registers (tl), indexed
+// like the K slots, from which the V loads, the masks and the end test read.
+template <int D>
 struct Loop {
+  static constexpr int NS = 4;
   static constexpr int KT = BN * D;   // elements of one K tile slot
   static constexpr int VT = D * BN;   // elements of one V^T tile slot
+  static constexpr uint32_t KSLOT = KT * 2, VSLOT = VT * 2;   // bytes
+  static constexpr int DMAS = LoadCtx<D>::PER_K + LoadCtx<D>::PER_V;
+
+  struct Args {
+    const AttnParams& p;
+    const LoadCtx<D>& lc;
+    uint16_t* lds;
+    int head, rng1, hg;
+    float sl2;
+    const int* kaddr;
+    const int* vaddr;
+    const bf16x8* qf;
+  };
 
   // Step j with J = j mod NS.  Scores of tile j are in s_cur.  Returns false
-  // after the last tile.  On the last tile the S(j+1) product runs on
-  // whatever the K slot holds and is discarded (cheaper than a branch in
-  // the scheduled block).
-  template <int J>
-  static __device__ __forceinline__ bool step(const AttnParams& p, uint16_t* lds, int head,
-                                              int rng1, Cursor& cc, Cursor& ck, Cursor& cv,
-                                              int& n_prev, int& n_cur, int& bad,
-                                              const int* kaddr, const int* vaddr,
-                                              const bf16x8* qf, f32x16* s_cur, f32x16* s_nxt,
-                                              f32x16* o, float& m_run, float* l_acc, int hg,
-                                              float sl2) {
-    uint16_t* kb = lds;
-    uint16_t* vb = lds + NS * KT;
-    n_prev = n_cur;
-    n_cur = 0;
-    if (ck.ri < rng1) {
-      const int n = load_k<D>(p, head, ck, kb + J * KT, bad);
-      if (n) n_cur += n;
-      else n_prev = n_cur = 0;
-      ck = cursor_next(p, rng1, ck);
+  // after the softmax of the last tile (its P V runs after the loop).  On
+  // the last tile the S(j+1) product runs on whatever the K slot holds and
+  // is discarded (cheaper than a branch in the scheduled block).
+  template <int J, bool LAG>
+  static __device__ __forceinline__ bool step(const Args& a, Walk& wk, Tile* tl, int& bad_u,
+                                              int& bad_v, int& last, f32x16* s_cur,
+                                              f32x16* s_nxt, bf16x8* pb, f32x16* o,
+                                              float& m_run, float* l_acc) {
+    const Tile tj = tl[J];   // tile j: its window masks S(j)
+    // the page read issued by the last step lands here, before any LDS read
+    // is in flight: a pending scalar load inside the compute block would
+    // force lgkmcnt(0) at every fragment read
+    asm volatile("" ::"s"(wk.page));
+    const Tile tk = walk_tile(a.p, a.rng1, wk, bad_u);   // tile j+4
+    walk_next(a.p, a.rng1, wk);
+    load_k<D, J * KSLOT>(a.p, a.lc, a.head, tk, a.lds, bad_v);
+    tl[J] = tk;
+    load_v<D, NS * KSLOT + ((J + 2) % NS) * VSLOT>(a.p, a.lc, a.head, tl[(J + 2) % NS], a.lds,
+                                                  bad_v);
+    if (tile_cut(tj)) {
+      int lo, hi;
+      tile_window(a.p, tj, lo, hi);
+      mask_tile<D>(s_cur, tile_kt(tj), lo, hi, a.hg);
     }
-    if (cv.ri < rng1) {
-      const int n = load_v<D>(p, head, cv, vb + ((J + NS - 1) % NS) * VT, bad);
-      if (n) n_cur += n;
-      else n_prev = n_cur = 0;
-      cv = cursor_next(p, rng1, cv);
+    softmax_qk<D>(a.lds + ((J + 1) % NS) * KT, a.kaddr, a.qf, s_cur, s_nxt, m_run, l_acc, a.sl2,
+                  pb);
+    if (tl[(J + 1) % NS].ktc < 0) {
+      last = J;   // P(j) V(j) of the last tile runs after the loop
+      return false;
     }
-    // let the page-table reads of the next step land here (scalar-cache
-    // hits): the use pins them above the compute block, where a pending
-    // scalar load would force lgkmcnt(0) at every LDS read
-    asm volatile("" ::"s"(ck.page), "s"(cv.page));
-    int w_lo, w_hi;
-    cursor_window(p, cc, w_lo, w_hi);
-    if (w_lo > cc.kt || w_hi < cc.kt + BN) mask_tile<D>(s_cur, cc.kt, w_lo, w_hi, hg);
-    compute_tile<D>(kb + ((J + 1) % NS) * KT, vb + J * VT, kaddr, vaddr, qf, s_cur, s_nxt, o,
-                    m_run, l_acc, sl2);
-    cc = cursor_next(p, rng1, cc);
-    if (cc.ri >= rng1) return false;
+    const uint16_t* vb = a.lds + NS * KT + J * VT;
+    float m_new;
+    if (!LAG && pv_max<D>(vb, a.vaddr, pb, o, s_nxt, m_run, a.sl2, m_new))
+      rescale<D>(o, l_acc, m_run, m_new);
     // a bare barrier: __syncthreads() would also drain every outstanding
     // load (its fence waits for vmcnt(0)), emptying the ring each step
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // register-path LDS stores
-    wait_vmcnt(NS >= 4 ? n_prev + n_cur : (NS == 3 ? n_cur : 0));
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(DMAS) : "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
+    if (LAG && pv_max<D>(vb, a.vaddr, pb, o, s_nxt, m_run, a.sl2, m_new))
+      rescale<D>(o, l_acc, m_run, m_new);
     return true;
   }
 
-  static __device__ __forceinline__ void run(const AttnParams& p, uint16_t* lds, int head,
-                                             int rng0, int rng1, const int* kaddr,
-                                             const int* vaddr, const bf16x8* qf, f32x16* o,
-                                             float& m_run, float* l_acc, int hg, float sl2,
-                                             int& bad) {
-    uint16_t* kb = lds;
-    uint16_t* vb = lds + NS * KT;
-    // prologue: K(0..NS-1) and V(0..NS-2), then S(0)
-    Cursor cc = cursor_first(p, rng0);
-    Cursor ck = cc, cv = cc;
-#pragma unroll
-    for (int i = 0; i < NS; ++i)
-      if (ck.ri < rng1) {
-        load_k<D>(p, head, ck, kb + i * KT, bad);
-        ck = cursor_next(p, rng1, ck);
-      }
-#pragma unroll
-    for (int i = 0; i < NS - 1; ++i)
-      if (cv.ri < rng1) {
-        load_v<D>(p, head, cv, vb + i * VT, bad);
-        cv = cursor_next(p, rng1, cv);
-      }
+  template <bool LAG>
+  static __device__ __forceinline__ void run(const Args& a, int rng0, f32x16* o, float& m_run,
+                                             float* l_acc, int& bad_u, int& bad_v) {
+    // prologue: K(0..3), V(0..1), then S(0) and the first running max
+    Walk wk = walk_first(a.p, rng0);
+    Tile tl[NS];
+#define WF_PRO_K(I)                                        \
+  tl[I] = walk_tile(a.p, a.rng1, wk, bad_u);               \
+  walk_next(a.p, a.rng1, wk);                              \
+  load_k<D, (I) * KSLOT>(a.p, a.lc, a.head, tl[I], a.lds, bad_v);
+    WF_PRO_K(0)
+    WF_PRO_K(1)
+    WF_PRO_K(2)
+    WF_PRO_K(3)
+#undef WF_PRO_K
+    load_v<D, NS * KSLOT>(a.p, a.lc, a.head, tl[0], a.lds, bad_v);
+    load_v<D, NS * KSLOT + VSLOT>(a.p, a.lc, a.head, tl[1], a.lds, bad_v);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     f32x16 sa[Frag<D>::SB], sb[Frag<D>::SB];
-    qk<D>(kb, kaddr, qf, sa);
-    // step 0 loads K(NS) into the slot of K(0): every wave must have read
+    qk<D>(a.lds, a.kaddr, a.qf, sa);
+    if (tile_cut(tl[0])) {
+      int lo, hi;
+      tile_window(a.p, tl[0], lo, hi);
+      mask_tile<D>(sa, tile_kt(tl[0]), lo, hi, a.hg);
+    }
+    // finite floor: a row with no visible key in the first tile keeps exact
+    // zero probabilities instead of -inf - -inf
+    m_run = fmaxf(tile_max<D>(sa, a.sl2), -1e30f);
+    // step 0 loads K(4) into the slot of K(0): every wave must have read
     // K(0) first (write-after-read across waves)
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    int n_prev = 0, n_cur = 0;
+    bf16x8 pb[Frag<D>::PK];
+    int last = 0;
     while (true) {
 #define WF_STEP(J, SC, SN)                                                                   \
-  if (J < NS && !step<J % NS>(p, lds, head, rng1, cc, ck, cv, n_prev, n_cur, bad, kaddr,     \
-                              vaddr, qf, SC, SN, o, m_run, l_acc, hg, sl2))                  \
-    break;
+  if (!step<J, LAG>(a, wk, tl, bad_u, bad_v, last, SC, SN, pb, o, m_run, l_acc)) break;
       WF_STEP(0, sa, sb)
       WF_STEP(1, sb, sa)
       WF_STEP(2, sa, sb)
       WF_STEP(3, sb, sa)
 #undef WF_STEP
-      static_assert(NS == 2 || NS == 4, "the unrolled ring assumes an even slot count <= 4");
     }
+    pv<D>(a.lds + NS * KT + last * VT, a.vaddr, pb, o);
     // no LDS-DMA may still be in flight when the block ends
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
 };
 
-template <int D, int NS>
+template <int D>
 __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_bf16(const AttnParams p) {
   constexpr int DK = Frag<D>::DK, DB = Frag<D>::DB, PK = Frag<D>::PK;
-  constexpr int KT = Loop<D, NS>::KT, VT = Loop<D, NS>::VT;
+  constexpr int NS = Loop<D>::NS, KT = Loop<D>::KT, VT = Loop<D>::VT;
   __shared__ __attribute__((aligned(16))) uint16_t lds[NS * (KT + VT)];
 
   const int tid = threadIdx.x;
@@ -597,15 +678,42 @@ void attn_fwd_bf16(const AttnParams p) {
     for (int t = 0; t < PK; ++t) vaddr[t] = ql * BN + ((2 * t) ^ vu) * 8;
   }
 
+  // block-constant load addressing
+  LoadCtx<D> lc;
+  {
+    const int ps = 1 << p.ps_log2;
+    const int64_t head_bytes = (int64_t)head * ps * D * 2;
+    lc.k_head = static_cast<const char*>(p.k_pages) + head_bytes;
+    lc.v_head = static_cast<const char*>(p.v_pages) + head_bytes;
+    lc.page_bytes = (int64_t)p.heads * ps * D * 2;
+    // K: chunk i of this thread is row r0 + i*NT/CPR, which has the same
+    // swizzle (a multiple of 16 rows further); V: feature row d0 + i*NT/8
+    constexpr int CPR = D / 8;
+    const int q = wave * 64 + lane;
+    const int r0 = q / CPR, kcol = (q % CPR) ^ kswz<D>(r0);
+#pragma unroll
+    for (int i = 0; i < LoadCtx<D>::PER_K; ++i)
+      lc.koff[i] = (uint32_t)((r0 + i * (NT / CPR)) * D + kcol * 8) * 2u;
+    const int d0 = q >> 3, vcol = (q & 7) ^ vswz(d0);
+#pragma unroll
+    for (int i = 0; i < LoadCtx<D>::PER_V; ++i)
+      lc.voff[i] = (uint32_t)((d0 + i * (NT / 8)) * ps + vcol * 8) * 2u;
+    lc.wave_lds = (uint32_t)(uintptr_t)lds + (uint32_t)__builtin_amdgcn_readfirstlane(wave) * 1024u;
+  }
+
   f32x16 o[DB];
 #pragma unroll
   for (int i = 0; i < DB; ++i) o[i] = f32x16{};
-  float m_run = -INFINITY;   // running max of scale*log2(e)*<q,k>
+  float m_run;               // running max of scale*log2(e)*<q,k>
   float l_acc[2] = {0.f, 0.f};
-  int bad = 0;
-  Loop<D, NS>::run(p, lds, head, rng0, rng1, kaddr, vaddr, qf, o, m_run, l_acc, hg,
-                   p.scale_log2, bad);
-  if (bad && threadIdx.x == 0) atomicOr(p.status, WF_STATUS_BAD_PAGE);
+  int bad_u = 0, bad_v = 0;  // bad page entries: wave-uniform and per-lane
+  const typename Loop<D>::Args args{p, lc, lds, head, rng1, hg, p.scale_log2, kaddr, vaddr, qf};
+  // waves NW/2.. run half a tile behind (see Loop)
+  if (wave >= NW / 2)
+    Loop<D>::template run<true>(args, rng0, o, m_run, l_acc, bad_u, bad_v);
+  else
+    Loop<D>::template run<false>(args, rng0, o, m_run, l_acc, bad_u, bad_v);
+  if ((bad_u | bad_v) && threadIdx.x == 0) atomicOr(p.status, WF_STATUS_BAD_PAGE);
 
   // ---- epilogue: O = O^T / l, LSE ------------------------------------------
   const float l = xhalf_sum(l_acc[0] + l_acc[1]);
@@ -634,8 +742,8 @@ hipError_t launch_attn_bf16(const AttnParams& p, int head_dim, int block_m,
                             hipStream_t stream) {
   if (block_m != BM) return hipErrorInvalidValue;
   dim3 grid(p.tiles_per_head * p.heads), block(NT);
-  if (head_dim == 128) hipLaunchKernelGGL((attn_fwd_bf16<128, kStages>), grid, block, 0, stream, p);
-  else hipLaunchKernelGGL((attn_fwd_bf16<64, kStages>), grid, block, 0, stream, p);
+  if (head_dim == 128) hipLaunchKernelGGL((attn_fwd_bf16<128>), grid, block, 0, stream, p);
+  else hipLaunchKernelGGL((attn_fwd_bf16<64>), grid, block, 0, stream, p);
   return hipGetLastError();
 }
 
