@@ -91,14 +91,13 @@ __device__ __forceinline__ int kswz(int r) {
 }
 __device__ __forceinline__ int vswz(int d) { return (d & 7) ^ ((d >> 3) & 1); }
 
-// Physical page of logical token L, or -1 (and `bad` set) for an entry
-// outside the pool.  The status word is written once, after the key loop.
+// Physical page for a page-table entry, or -1 (and `bad` set) for an entry
+// outside the pool; integer arithmetic only, so that a uniform entry stays
+// in scalar registers.  The status word is written once, after the key loop.
 __device__ __forceinline__ int check_page(const AttnParams& p, int page, int& bad) {
-  if (page < 0 || page >= p.num_pages) {
-    bad = 1;
-    return -1;
-  }
-  return page;
+  const int out = (unsigned)page >= (unsigned)p.num_pages;
+  bad |= out;
+  return out ? -1 : page;
 }
 
 // Per-lane lookup (register path: the token may differ between lanes).
@@ -138,17 +137,22 @@ struct Tile {
   int page;
 };
 
+// BP: pages hold at least BN keys, so a 64-aligned tile lies in one page
+// (otherwise every tile takes the register path, with per-lane lookups).
+template <bool BP>
 __device__ __forceinline__ void walk_page(const AttnParams& p, Walk& w) {
-  if (p.ps_log2 >= 6) w.page = table_entry(p, w.kt >> p.ps_log2);
+  if (BP) w.page = table_entry(p, w.kt >> p.ps_log2);
 }
 
+template <bool BP>
 __device__ __forceinline__ Walk walk_first(const AttnParams& p, int rng0) {
   const int2 r = p.ranges[rng0];
   Walk w{rng0, r.x & ~(BN - 1), r.x, r.y, -1};
-  walk_page(p, w);
+  walk_page<BP>(p, w);
   return w;
 }
 
+template <bool BP>
 __device__ __forceinline__ void walk_next(const AttnParams& p, int rng1, Walk& w) {
   w.kt += BN;
   if (w.kt >= w.rhi) {
@@ -158,15 +162,18 @@ __device__ __forceinline__ void walk_next(const AttnParams& p, int rng1, Walk& w
     w.rhi = r.y;
     w.kt = r.x & ~(BN - 1);
   }
-  walk_page(p, w);
+  walk_page<BP>(p, w);
 }
 
 // The tile at the walk position; its page entry is checked here, once.
+// The cut flag is integer arithmetic (sign bits), not a boolean, so that it
+// stays in scalar registers.
+template <bool BP>
 __device__ __forceinline__ Tile walk_tile(const AttnParams& p, int rng1, const Walk& w,
                                           int& bad) {
   if (w.ri >= rng1) return Tile{-1, 0, -1};
-  const int page = p.ps_log2 >= 6 ? check_page(p, w.page, bad) : -1;
-  const int cut = (w.kt < w.rlo || w.kt + BN > w.rhi) ? 1 : 0;
+  const int page = BP ? check_page(p, w.page, bad) : -1;
+  const int cut = (int)(((uint32_t)(w.kt - w.rlo) | (uint32_t)(w.rhi - (w.kt + BN))) >> 31);
   return Tile{w.kt | cut, w.ri, page};
 }
 
@@ -182,7 +189,9 @@ __device__ __forceinline__ void tile_window(const AttnParams& p, const Tile& t, 
 }
 
 // every key of the tile visible and on one good page: the direct-load path
-__device__ __forceinline__ bool tile_full(const Tile& t) { return t.page >= 0 && !tile_cut(t); }
+__device__ __forceinline__ bool tile_full(const Tile& t) {
+  return ((t.page >> 31) | (t.ktc & 1)) == 0;
+}
 
 // Block-constant addressing of the loads.  The K page [H][ps][D] and the
 // V page [H][D][ps] of one head have the same size, so one page stride and
@@ -236,7 +245,7 @@ __device__ __forceinline__ void dma_chunks(const char* base, const uint32_t* off
 // other tile takes the register path, and a tile past the end of the walk
 // loads nothing; both end with every older vector load complete, so a step
 // never has more than its own direct loads outstanding.
-template <int D, uint32_t SLOT>
+template <int D, bool BP, uint32_t SLOT>
 __device__ __forceinline__ void load_k(const AttnParams& p, const LoadCtx<D>& lc, int head,
                                        const Tile& t, uint16_t* __restrict__ lds, int& bad) {
   constexpr int CPR = D / 8;   // chunks per K row
@@ -259,7 +268,6 @@ __device__ __forceinline__ void load_k(const AttnParams& p, const LoadCtx<D>& lc
     uint16_t* kbuf = lds + SLOT / 2;
     const uint4 nan8 = make_uint4(0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u);
     const uint4 zero = make_uint4(0, 0, 0, 0);
-    const bool one_page = p.ps_log2 >= 6;
     int lo, hi;
     tile_window(p, t, lo, hi);
 #pragma unroll 1
@@ -269,7 +277,7 @@ __device__ __forceinline__ void load_k(const AttnParams& p, const LoadCtx<D>& lc
       const int L = tile_kt(t) + r;
       uint4 val = nan8;
       if (L >= lo && L < hi) {
-        const int page = one_page ? t.page : lookup_page(p, L, bad);
+        const int page = BP ? t.page : lookup_page(p, L, bad);
         val = zero;
         if (page >= 0)
           val = *reinterpret_cast<const uint4*>(
@@ -283,7 +291,7 @@ __device__ __forceinline__ void load_k(const AttnParams& p, const LoadCtx<D>& lc
 
 // ---- global -> LDS: the V^T tile [D][BN] of one head -----------------------
 // Same contract as load_k.
-template <int D, uint32_t SLOT>
+template <int D, bool BP, uint32_t SLOT>
 __device__ __forceinline__ void load_v(const AttnParams& p, const LoadCtx<D>& lc, int head,
                                        const Tile& t, uint16_t* __restrict__ lds, int& bad) {
   constexpr int PER = LoadCtx<D>::PER_V;
@@ -299,7 +307,6 @@ __device__ __forceinline__ void load_v(const AttnParams& p, const LoadCtx<D>& lc
     const uint16_t* __restrict__ vpg = static_cast<const uint16_t*>(p.v_pages);
     uint16_t* vbuf = lds + SLOT / 2;
     const uint4 zero = make_uint4(0, 0, 0, 0);
-    const bool one_page = p.ps_log2 >= 6;
     int lo, hi;
     tile_window(p, t, lo, hi);
 #pragma unroll 1
@@ -310,7 +317,7 @@ __device__ __forceinline__ void load_v(const AttnParams& p, const LoadCtx<D>& lc
       uint4 val = zero;
       if (L + 8 > lo && L < hi) {
         // an 8-key run never crosses a page (page_size >= 16, runs 8-aligned)
-        const int page = one_page ? t.page : lookup_page(p, max(L, lo), bad);
+        const int page = BP ? t.page : lookup_page(p, max(L, lo), bad);
         if (page >= 0) {
           val = *reinterpret_cast<const uint4*>(
               vpg + (((int64_t)page * p.heads + head) * D + d) * ps + (L & (ps - 1)));
@@ -514,7 +521,7 @@ __device__ __forceinline__ void rescale(f32x16* o, float* l_acc, float& m_run, f
 // The walk runs once per step, four tiles ahead (for K); the tiles in
 // between are kept in a four-entry ring in scalar registers (tl), indexed
 // like the K slots, from which the V loads, the masks and the end test read.
-template <int D>
+template <int D, bool BP>
 struct Loop {
   static constexpr int NS = 4;
   static constexpr int KT = BN * D;   // elements of one K tile slot
@@ -547,12 +554,12 @@ struct Loop {
     // is in flight: a pending scalar load inside the compute block would
     // force lgkmcnt(0) at every fragment read
     asm volatile("" ::"s"(wk.page));
-    const Tile tk = walk_tile(a.p, a.rng1, wk, bad_u);   // tile j+4
-    walk_next(a.p, a.rng1, wk);
-    load_k<D, J * KSLOT>(a.p, a.lc, a.head, tk, a.lds, bad_v);
+    const Tile tk = walk_tile<BP>(a.p, a.rng1, wk, bad_u);   // tile j+4
+    walk_next<BP>(a.p, a.rng1, wk);
+    load_k<D, BP, J * KSLOT>(a.p, a.lc, a.head, tk, a.lds, bad_v);
     tl[J] = tk;
-    load_v<D, NS * KSLOT + ((J + 2) % NS) * VSLOT>(a.p, a.lc, a.head, tl[(J + 2) % NS], a.lds,
-                                                  bad_v);
+    load_v<D, BP, NS * KSLOT + ((J + 2) % NS) * VSLOT>(a.p, a.lc, a.head, tl[(J + 2) % NS],
+                                                      a.lds, bad_v);
     if (tile_cut(tj)) {
       int lo, hi;
       tile_window(a.p, tj, lo, hi);
@@ -583,19 +590,19 @@ struct Loop {
   static __device__ __forceinline__ void run(const Args& a, int rng0, f32x16* o, float& m_run,
                                              float* l_acc, int& bad_u, int& bad_v) {
     // prologue: K(0..3), V(0..1), then S(0) and the first running max
-    Walk wk = walk_first(a.p, rng0);
+    Walk wk = walk_first<BP>(a.p, rng0);
     Tile tl[NS];
 #define WF_PRO_K(I)                                        \
-  tl[I] = walk_tile(a.p, a.rng1, wk, bad_u);               \
-  walk_next(a.p, a.rng1, wk);                              \
-  load_k<D, (I) * KSLOT>(a.p, a.lc, a.head, tl[I], a.lds, bad_v);
+  tl[I] = walk_tile<BP>(a.p, a.rng1, wk, bad_u);           \
+  walk_next<BP>(a.p, a.rng1, wk);                          \
+  load_k<D, BP, (I) * KSLOT>(a.p, a.lc, a.head, tl[I], a.lds, bad_v);
     WF_PRO_K(0)
     WF_PRO_K(1)
     WF_PRO_K(2)
     WF_PRO_K(3)
 #undef WF_PRO_K
-    load_v<D, NS * KSLOT>(a.p, a.lc, a.head, tl[0], a.lds, bad_v);
-    load_v<D, NS * KSLOT + VSLOT>(a.p, a.lc, a.head, tl[1], a.lds, bad_v);
+    load_v<D, BP, NS * KSLOT>(a.p, a.lc, a.head, tl[0], a.lds, bad_v);
+    load_v<D, BP, NS * KSLOT + VSLOT>(a.p, a.lc, a.head, tl[1], a.lds, bad_v);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     f32x16 sa[Frag<D>::SB], sb[Frag<D>::SB];
@@ -630,11 +637,12 @@ struct Loop {
   }
 };
 
-template <int D>
+template <int D, bool BP>
 __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_bf16(const AttnParams p) {
+  using L = Loop<D, BP>;
   constexpr int DK = Frag<D>::DK, DB = Frag<D>::DB, PK = Frag<D>::PK;
-  constexpr int NS = Loop<D>::NS, KT = Loop<D>::KT, VT = Loop<D>::VT;
+  constexpr int NS = L::NS, KT = L::KT, VT = L::VT;
   __shared__ __attribute__((aligned(16))) uint16_t lds[NS * (KT + VT)];
 
   const int tid = threadIdx.x;
@@ -707,12 +715,12 @@ void attn_fwd_bf16(const AttnParams p) {
   float m_run;               // running max of scale*log2(e)*<q,k>
   float l_acc[2] = {0.f, 0.f};
   int bad_u = 0, bad_v = 0;  // bad page entries: wave-uniform and per-lane
-  const typename Loop<D>::Args args{p, lc, lds, head, rng1, hg, p.scale_log2, kaddr, vaddr, qf};
+  const typename L::Args args{p, lc, lds, head, rng1, hg, p.scale_log2, kaddr, vaddr, qf};
   // waves NW/2.. run half a tile behind (see Loop)
   if (wave >= NW / 2)
-    Loop<D>::template run<true>(args, rng0, o, m_run, l_acc, bad_u, bad_v);
+    L::template run<true>(args, rng0, o, m_run, l_acc, bad_u, bad_v);
   else
-    Loop<D>::template run<false>(args, rng0, o, m_run, l_acc, bad_u, bad_v);
+    L::template run<false>(args, rng0, o, m_run, l_acc, bad_u, bad_v);
   if ((bad_u | bad_v) && threadIdx.x == 0) atomicOr(p.status, WF_STATUS_BAD_PAGE);
 
   // ---- epilogue: O = O^T / l, LSE ------------------------------------------
@@ -742,8 +750,14 @@ hipError_t launch_attn_bf16(const AttnParams& p, int head_dim, int block_m,
                             hipStream_t stream) {
   if (block_m != BM) return hipErrorInvalidValue;
   dim3 grid(p.tiles_per_head * p.heads), block(NT);
-  if (head_dim == 128) hipLaunchKernelGGL((attn_fwd_bf16<128>), grid, block, 0, stream, p);
-  else hipLaunchKernelGGL((attn_fwd_bf16<64>), grid, block, 0, stream, p);
+  const bool bp = p.ps_log2 >= 6;   // pages of >= BN keys
+  if (head_dim == 128) {
+    if (bp) hipLaunchKernelGGL((attn_fwd_bf16<128, true>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((attn_fwd_bf16<128, false>), grid, block, 0, stream, p);
+  } else {
+    if (bp) hipLaunchKernelGGL((attn_fwd_bf16<64, true>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((attn_fwd_bf16<64, false>), grid, block, 0, stream, p);
+  }
   return hipGetLastError();
 }
 
