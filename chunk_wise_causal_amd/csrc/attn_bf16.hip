@@ -66,6 +66,7 @@ constexpr int NW = 8;       // waves per block, 32 query rows each
 constexpr int BM = 32 * NW; // query rows per block
 constexpr int BN = 64;      // keys per tile
 constexpr int NT = 64 * NW; // threads per block
+constexpr int LT = NT / 2;  // threads that issue the K/V tile loads (waves 0..NW/2-1)
 constexpr float kRescaleSlack = 8.0f;   // log2 units
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -193,13 +194,14 @@ __device__ __forceinline__ bool tile_full(const Tile& t) {
   return ((t.page >> 31) | (t.ktc & 1)) == 0;
 }
 
-// Block-constant addressing of the loads.  The K page [H][ps][D] and the
-// V page [H][D][ps] of one head have the same size, so one page stride and
-// one per-head offset serve both.
+// Block-constant addressing of the loads, which the first LT threads issue
+// (the waves that run ahead; see Loop).  The K page [H][ps][D] and the V
+// page [H][D][ps] of one head have the same size, so one page stride and one
+// per-head offset serve both.
 template <int D>
 struct LoadCtx {
-  static constexpr int PER_K = BN * (D / 8) / NT;   // 16-byte chunks per thread
-  static constexpr int PER_V = D * (BN / 8) / NT;
+  static constexpr int PER_K = BN * (D / 8) / LT;   // 16-byte chunks per thread
+  static constexpr int PER_V = D * (BN / 8) / LT;
   const char* k_head;       // K pages + head offset (bytes)
   const char* v_head;
   int64_t page_bytes;
@@ -229,13 +231,13 @@ __device__ __forceinline__ void dma16(const char* sbase, uint32_t voff, uint32_t
       : "memory", "m0", "scc");
 }
 
-// The PER chunks of one thread: chunk i goes to this wave's 1 KB run i*NW
-// runs further on.
+// The PER chunks of one thread: chunk i goes to this wave's 1 KB run
+// i*LT/64 runs further on.
 template <uint32_t SLOT, int I, int PER>
 __device__ __forceinline__ void dma_chunks(const char* base, const uint32_t* off,
                                            uint32_t wave_lds) {
   if constexpr (I < PER) {
-    dma16<SLOT + I * NW * 1024>(base, off[I], wave_lds);
+    dma16<SLOT + I * (LT / 64) * 1024>(base, off[I], wave_lds);
     dma_chunks<SLOT, I + 1, PER>(base, off, wave_lds);
   }
 }
@@ -272,7 +274,7 @@ __device__ __forceinline__ void load_k(const AttnParams& p, const LoadCtx<D>& lc
     tile_window(p, t, lo, hi);
 #pragma unroll 1
     for (int i = 0; i < PER; ++i) {
-      const int q = i * NT + tid;
+      const int q = i * LT + tid;
       const int r = q / CPR, col = (q % CPR) ^ kswz<D>(r);
       const int L = tile_kt(t) + r;
       uint4 val = nan8;
@@ -311,7 +313,7 @@ __device__ __forceinline__ void load_v(const AttnParams& p, const LoadCtx<D>& lc
     tile_window(p, t, lo, hi);
 #pragma unroll 1
     for (int i = 0; i < PER; ++i) {
-      const int q = i * NT + tid;
+      const int q = i * LT + tid;
       const int d = q >> 3, col = (q & 7) ^ vswz(d);
       const int L = tile_kt(t) + col * 8;   // first of the chunk's 8 keys
       uint4 val = zero;
@@ -514,10 +516,13 @@ __device__ __forceinline__ void rescale(f32x16* o, float* l_acc, float& m_run, f
 // the matrix pipe busy.
 // At tile j the slots hold K(j+1..j+4) and V(j-1..j+2); step j issues
 // K(j+4) into the slot of K(j) and V(j+2) into the slot of V(j-2), both read
-// by every wave before the previous barrier.  The barrier of step j must
-// publish K(j+2) and V(j+1), issued in earlier steps: each wave waits until
-// no more than this step's direct loads are outstanding (vector loads
-// complete in order), then the barrier publishes them to all waves.
+// by every wave before the previous barrier.  Only the leading waves issue
+// loads: they finish their half-tiles early and would otherwise idle at the
+// barrier, while the lagging waves' softmax is the critical path.  The
+// barrier of step j must publish K(j+2) and V(j+1), issued in earlier steps:
+// each loading wave waits until no more than this step's direct loads are
+// outstanding (vector loads complete in order), then the barrier publishes
+// them to all waves.
 // The walk runs once per step, four tiles ahead (for K); the tiles in
 // between are kept in a four-entry ring in scalar registers (tl), indexed
 // like the K slots, from which the V loads, the masks and the end test read.
@@ -527,7 +532,7 @@ struct Loop {
   static constexpr int KT = BN * D;   // elements of one K tile slot
   static constexpr int VT = D * BN;   // elements of one V^T tile slot
   static constexpr uint32_t KSLOT = KT * 2, VSLOT = VT * 2;   // bytes
-  static constexpr int DMAS = LoadCtx<D>::PER_K + LoadCtx<D>::PER_V;
+  static constexpr int DMAS = LoadCtx<D>::PER_K + LoadCtx<D>::PER_V;   // per loading thread
 
   struct Args {
     const AttnParams& p;
@@ -556,10 +561,12 @@ struct Loop {
     asm volatile("" ::"s"(wk.page));
     const Tile tk = walk_tile<BP>(a.p, a.rng1, wk, bad_u);   // tile j+4
     walk_next<BP>(a.p, a.rng1, wk);
-    load_k<D, BP, J * KSLOT>(a.p, a.lc, a.head, tk, a.lds, bad_v);
+    if (!LAG) {
+      load_k<D, BP, J * KSLOT>(a.p, a.lc, a.head, tk, a.lds, bad_v);
+      load_v<D, BP, NS * KSLOT + ((J + 2) % NS) * VSLOT>(a.p, a.lc, a.head, tl[(J + 2) % NS],
+                                                        a.lds, bad_v);
+    }
     tl[J] = tk;
-    load_v<D, BP, NS * KSLOT + ((J + 2) % NS) * VSLOT>(a.p, a.lc, a.head, tl[(J + 2) % NS],
-                                                      a.lds, bad_v);
     if (tile_cut(tj)) {
       int lo, hi;
       tile_window(a.p, tj, lo, hi);
@@ -578,7 +585,7 @@ struct Loop {
     // a bare barrier: __syncthreads() would also drain every outstanding
     // load (its fence waits for vmcnt(0)), emptying the ring each step
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // register-path LDS stores
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(DMAS) : "memory");
+    if (!LAG) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(DMAS) : "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     if (LAG && pv_max<D>(vb, a.vaddr, pb, o, s_nxt, m_run, a.sl2, m_new))
@@ -592,17 +599,19 @@ struct Loop {
     // prologue: K(0..3), V(0..1), then S(0) and the first running max
     Walk wk = walk_first<BP>(a.p, rng0);
     Tile tl[NS];
-#define WF_PRO_K(I)                                        \
-  tl[I] = walk_tile<BP>(a.p, a.rng1, wk, bad_u);           \
-  walk_next<BP>(a.p, a.rng1, wk);                          \
-  load_k<D, BP, (I) * KSLOT>(a.p, a.lc, a.head, tl[I], a.lds, bad_v);
+#define WF_PRO_K(I)                                                          \
+  tl[I] = walk_tile<BP>(a.p, a.rng1, wk, bad_u);                             \
+  walk_next<BP>(a.p, a.rng1, wk);                                            \
+  if (!LAG) load_k<D, BP, (I) * KSLOT>(a.p, a.lc, a.head, tl[I], a.lds, bad_v);
     WF_PRO_K(0)
     WF_PRO_K(1)
     WF_PRO_K(2)
     WF_PRO_K(3)
 #undef WF_PRO_K
-    load_v<D, BP, NS * KSLOT>(a.p, a.lc, a.head, tl[0], a.lds, bad_v);
-    load_v<D, BP, NS * KSLOT + VSLOT>(a.p, a.lc, a.head, tl[1], a.lds, bad_v);
+    if (!LAG) {
+      load_v<D, BP, NS * KSLOT>(a.p, a.lc, a.head, tl[0], a.lds, bad_v);
+      load_v<D, BP, NS * KSLOT + VSLOT>(a.p, a.lc, a.head, tl[1], a.lds, bad_v);
+    }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     f32x16 sa[Frag<D>::SB], sb[Frag<D>::SB];
@@ -694,18 +703,20 @@ void attn_fwd_bf16(const AttnParams p) {
     lc.k_head = static_cast<const char*>(p.k_pages) + head_bytes;
     lc.v_head = static_cast<const char*>(p.v_pages) + head_bytes;
     lc.page_bytes = (int64_t)p.heads * ps * D * 2;
-    // K: chunk i of this thread is row r0 + i*NT/CPR, which has the same
-    // swizzle (a multiple of 16 rows further); V: feature row d0 + i*NT/8
+    // K: chunk i of a loading thread is row r0 + i*LT/CPR, which has the
+    // same swizzle (a multiple of 16 rows further); V: feature row
+    // d0 + i*LT/8 (also a multiple of 16 further)
     constexpr int CPR = D / 8;
-    const int q = wave * 64 + lane;
+    static_assert((LT / CPR) % 16 == 0 && (LT / 8) % 16 == 0, "chunk rows keep their swizzle");
+    const int q = (wave % (LT / 64)) * 64 + lane;
     const int r0 = q / CPR, kcol = (q % CPR) ^ kswz<D>(r0);
 #pragma unroll
     for (int i = 0; i < LoadCtx<D>::PER_K; ++i)
-      lc.koff[i] = (uint32_t)((r0 + i * (NT / CPR)) * D + kcol * 8) * 2u;
+      lc.koff[i] = (uint32_t)((r0 + i * (LT / CPR)) * D + kcol * 8) * 2u;
     const int d0 = q >> 3, vcol = (q & 7) ^ vswz(d0);
 #pragma unroll
     for (int i = 0; i < LoadCtx<D>::PER_V; ++i)
-      lc.voff[i] = (uint32_t)((d0 + i * (NT / 8)) * ps + vcol * 8) * 2u;
+      lc.voff[i] = (uint32_t)((d0 + i * (LT / 8)) * ps + vcol * 8) * 2u;
     lc.wave_lds = (uint32_t)(uintptr_t)lds + (uint32_t)__builtin_amdgcn_readfirstlane(wave) * 1024u;
   }
 
@@ -721,7 +732,10 @@ void attn_fwd_bf16(const AttnParams p) {
     L::template run<true>(args, rng0, o, m_run, l_acc, bad_u, bad_v);
   else
     L::template run<false>(args, rng0, o, m_run, l_acc, bad_u, bad_v);
-  if ((bad_u | bad_v) && threadIdx.x == 0) atomicOr(p.status, WF_STATUS_BAD_PAGE);
+  // one status write per wave that met a bad page entry (per-lane lookups
+  // of the register path included)
+  if ((bad_u | (__builtin_amdgcn_ballot_w64(bad_v != 0) != 0)) && lane == 0)
+    atomicOr(p.status, WF_STATUS_BAD_PAGE);
 
   // ---- epilogue: O = O^T / l, LSE ------------------------------------------
   const float l = xhalf_sum(l_acc[0] + l_acc[1]);
