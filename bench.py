@@ -242,7 +242,7 @@ def main():
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic_from_profiles(kernel_source_hash()),
-                     "kernel": "attn_fwd_bf16<128>"},
+                     "kernel": "attn_fwd_bf16<128, true>"},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
