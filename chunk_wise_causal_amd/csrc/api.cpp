@@ -87,6 +87,92 @@ int check_rows(const char* name, const void* ptr, int64_t stride, const wf_kv_po
 
 }  // namespace
 
+namespace {
+
+// One query group of an attention launch: its rows and its merged visible
+// key ranges (sorted, non-adjacent).
+struct GroupSpec {
+  int row0, row1;
+  std::vector<int2> ranges;
+  int64_t vis;   // visible keys
+};
+
+// Append [lo, hi) to sorted ranges, merging with the last one when adjacent.
+void push_range(std::vector<int2>& r, int lo, int hi) {
+  if (!r.empty() && r.back().y == lo) r.back().y = hi;
+  else r.push_back(make_int2(lo, hi));
+}
+
+// The launch shared by the slot and the generic entry points: groups are
+// validated and their ranges merged by the caller; q and out were checked
+// when any group has rows.
+int launch_groups(const wf_kv_pool* pool, const std::vector<GroupSpec>& groups, const void* q,
+                  int64_t q_row_stride, float scale, void* out, int64_t out_row_stride,
+                  float* lse, int64_t lse_stride, hipStream_t stream) {
+  int n_ranges = 0;
+  bool any_rows = false;
+  for (const GroupSpec& g : groups) {
+    n_ranges += (int)g.ranges.size();
+    any_rows |= g.row1 > g.row0;
+  }
+  if (n_ranges > wf::kMaxRanges)
+    return fail(WF_ERR_UNSUPPORTED, "%d visible ranges exceed the limit of %d", n_ranges,
+                wf::kMaxRanges);
+  if (!any_rows) return ok();
+
+  wf::AttnParams p{};
+  const bool bf16 = pool->dtype == WF_BF16;
+  const int bm = bf16 ? wf::kBlockMBf16 : wf::kBlockMFp32;
+  // longest visible context first (largest tiles start first), ties by group
+  std::vector<int> order(groups.size());
+  for (size_t g = 0; g < groups.size(); ++g) order[g] = (int)g;
+  std::stable_sort(order.begin(), order.end(),
+                   [&](int a, int b) { return groups[a].vis > groups[b].vis; });
+  int nr = 0, tiles = 0, k = 0;
+  for (int gi : order) {
+    const GroupSpec& g = groups[gi];
+    const int rows = g.row1 - g.row0;
+    if (rows == 0) continue;
+    tiles += (rows + bm - 1) / bm;
+    p.grp_tile_end[k] = tiles;
+    p.grp_row0[k] = g.row0;
+    p.grp_row1[k] = g.row1;
+    p.grp_rng0[k] = nr;
+    for (const int2& r : g.ranges) p.ranges[nr++] = r;
+    p.grp_rng1[k] = nr;
+    ++k;
+  }
+  p.n_groups = k;
+  p.tiles_per_head = tiles;
+  p.q = q;
+  p.out = out;
+  p.lse = lse;
+  p.k_pages = pool->k_pages;
+  p.v_pages = pool->v_pages;
+  p.page_table = pool->page_table;
+  p.q_stride = q_row_stride;
+  p.out_stride = out_row_stride;
+  p.heads = pool->num_heads;
+  p.ps_log2 = log2_exact(pool->page_size);
+  p.num_pages = pool->num_pages;
+  p.num_logical_pages = pool->num_logical_pages;
+  p.lse_stride = (int32_t)lse_stride;
+  p.scale = scale;
+  p.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  const int64_t blocks = (int64_t)tiles * pool->num_heads;
+  if (blocks > 0x7fffffff) return fail(WF_ERR_UNSUPPORTED, "too many query tiles");
+
+  hipError_t e;
+  p.status = wf::status_word_ptr(&e);
+  if (!p.status) return hip_fail(e, "status word");
+  e = bf16 ? wf::launch_attn_bf16(p, pool->head_dim, bm, stream)
+           : wf::launch_attn_fp32(p, pool->head_dim, bm, stream);
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  return ok();
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* wf_last_error(void) { return g_err.c_str(); }
@@ -236,75 +322,90 @@ int wf_chunk_attn(const wf_kv_pool* pool, const wf_segment* segs, int32_t n_segs
   }
 
   // ---- slot-mask schedule: merged visible ranges per group ([WF] §3.1) ----
-  wf::AttnParams p{};
-  struct G { int g; int64_t vis; };
-  std::vector<G> order;
-  std::vector<std::vector<int2>> granges(n_slots);
-  int n_ranges = 0;
+  std::vector<GroupSpec> groups(n_slots);
   for (int g = 0; g < n_slots; ++g) {
-    const int s = first_slot + g;
-    std::vector<int2>& r = granges[g];
-    int64_t vis = 0;
+    const int sl = first_slot + g;
+    GroupSpec& G = groups[g];
+    G.row0 = q_slot_start[g];
+    G.row1 = q_slot_start[g + 1];
+    G.vis = 0;
     for (const wf_segment& sg : sorted) {
-      if (!(sg.slot < 0 || sg.slot >= s)) continue;
-      const int lo = sg.kv_start, hi = sg.kv_start + sg.kv_len;
-      vis += hi - lo;
-      if (!r.empty() && r.back().y == lo) r.back().y = hi;
-      else r.push_back(make_int2(lo, hi));
+      if (!(sg.slot < 0 || sg.slot >= sl)) continue;
+      G.vis += sg.kv_len;
+      push_range(G.ranges, sg.kv_start, sg.kv_start + sg.kv_len);
     }
-    n_ranges += (int)r.size();
-    order.push_back({g, vis});
   }
-  if (n_ranges > wf::kMaxRanges)
-    return fail(WF_ERR_UNSUPPORTED, "%d visible ranges exceed the limit of %d", n_ranges,
-                wf::kMaxRanges);
-  if (!any_rows) return ok();
+  return launch_groups(pool, groups, q, q_row_stride, scale, out, out_row_stride, lse,
+                       total_rows, stream);
+}
 
-  const bool bf16 = pool->dtype == WF_BF16;
-  const int bm = bf16 ? wf::kBlockMBf16 : wf::kBlockMFp32;
-  // longest visible context first (largest tiles start first), ties by group
-  std::stable_sort(order.begin(), order.end(),
-                   [](const G& a, const G& b) { return a.vis > b.vis; });
-  int nr = 0, tiles = 0, k = 0;
-  for (const G& o : order) {
-    const int rows = q_slot_start[o.g + 1] - q_slot_start[o.g];
-    if (rows == 0) continue;
-    tiles += (rows + bm - 1) / bm;
-    p.grp_tile_end[k] = tiles;
-    p.grp_row0[k] = q_slot_start[o.g];
-    p.grp_row1[k] = q_slot_start[o.g + 1];
-    p.grp_rng0[k] = nr;
-    for (const int2& r : granges[o.g]) p.ranges[nr++] = r;
-    p.grp_rng1[k] = nr;
-    ++k;
+int wf_group_attn(const wf_kv_pool* pool, const wf_kv_run* runs, int32_t n_runs,
+                  const wf_query_group* groups, int32_t n_groups, const void* q,
+                  int64_t q_row_stride, float scale, void* out, int64_t out_row_stride,
+                  float* lse, int64_t lse_stride, hipStream_t stream) {
+  int rc = check_pool(pool);
+  if (rc) return rc;
+  if (!runs) return fail(WF_ERR_INVALID, "runs is NULL");
+  if (n_runs < 1 || n_runs > wf::kMaxRanges)
+    return fail(WF_ERR_INVALID, "n_runs %d not in [1, %d]", n_runs, wf::kMaxRanges);
+  if (!groups) return fail(WF_ERR_INVALID, "groups is NULL");
+  if (n_groups < 1 || n_groups > wf::kMaxGroups)
+    return fail(WF_ERR_INVALID, "n_groups %d not in [1, %d]", n_groups, wf::kMaxGroups);
+  if (!(scale > 0.f) || !std::isfinite(scale))
+    return fail(WF_ERR_INVALID, "scale must be finite and > 0");
+  const int64_t cap = (int64_t)pool->num_logical_pages * pool->page_size;
+  for (int i = 0; i < n_runs; ++i) {
+    const wf_kv_run& r = runs[i];
+    if (r.kv_len < 1 || r.kv_start < 0 || (int64_t)r.kv_start + r.kv_len > cap)
+      return fail(WF_ERR_INVALID, "run %d [%d, +%d) outside the pool's %lld tokens", i,
+                  r.kv_start, r.kv_len, (long long)cap);
   }
-  p.n_groups = k;
-  p.tiles_per_head = tiles;
-  p.q = q;
-  p.out = out;
-  p.lse = lse;
-  p.k_pages = pool->k_pages;
-  p.v_pages = pool->v_pages;
-  p.page_table = pool->page_table;
-  p.q_stride = q_row_stride;
-  p.out_stride = out_row_stride;
-  p.heads = pool->num_heads;
-  p.ps_log2 = log2_exact(pool->page_size);
-  p.num_pages = pool->num_pages;
-  p.num_logical_pages = pool->num_logical_pages;
-  p.lse_stride = total_rows;
-  p.scale = scale;
-  p.scale_log2 = (float)((double)scale * 1.4426950408889634);
-  const int64_t blocks = (int64_t)tiles * pool->num_heads;
-  if (blocks > 0x7fffffff) return fail(WF_ERR_UNSUPPORTED, "too many query tiles");
-
-  hipError_t e;
-  p.status = wf::status_word_ptr(&e);
-  if (!p.status) return hip_fail(e, "status word");
-  e = bf16 ? wf::launch_attn_bf16(p, pool->head_dim, bm, stream)
-           : wf::launch_attn_fp32(p, pool->head_dim, bm, stream);
-  if (e != hipSuccess) return hip_fail(e, "attention launch");
-  return ok();
+  int64_t max_row = 0;
+  bool any_rows = false;
+  std::vector<GroupSpec> specs(n_groups);
+  for (int g = 0; g < n_groups; ++g) {
+    const wf_query_group& G = groups[g];
+    if (G.q_row_start < 0 || G.q_row_end < G.q_row_start)
+      return fail(WF_ERR_INVALID, "group %d rows [%d, %d) invalid", g, G.q_row_start,
+                  G.q_row_end);
+    if (G.run_begin < 0 || G.run_end <= G.run_begin || G.run_end > n_runs)
+      return fail(WF_ERR_INVALID, "group %d runs [%d, %d) not inside [0, %d) or empty", g,
+                  G.run_begin, G.run_end, n_runs);
+    std::vector<wf_kv_run> mine(runs + G.run_begin, runs + G.run_end);
+    std::sort(mine.begin(), mine.end(),
+              [](const wf_kv_run& a, const wf_kv_run& b) { return a.kv_start < b.kv_start; });
+    GroupSpec& S = specs[g];
+    S.row0 = G.q_row_start;
+    S.row1 = G.q_row_end;
+    S.vis = 0;
+    for (size_t i = 0; i < mine.size(); ++i) {
+      if (i && (int64_t)mine[i - 1].kv_start + mine[i - 1].kv_len > mine[i].kv_start)
+        return fail(WF_ERR_INVALID, "runs of group %d overlap at token %d", g, mine[i].kv_start);
+      S.vis += mine[i].kv_len;
+      push_range(S.ranges, mine[i].kv_start, mine[i].kv_start + mine[i].kv_len);
+    }
+    max_row = std::max<int64_t>(max_row, G.q_row_end);
+    any_rows |= G.q_row_end > G.q_row_start;
+  }
+  // each output row is written by one group only
+  std::vector<std::pair<int, int>> rows;
+  for (int g = 0; g < n_groups; ++g)
+    if (groups[g].q_row_end > groups[g].q_row_start)
+      rows.push_back({groups[g].q_row_start, groups[g].q_row_end});
+  std::sort(rows.begin(), rows.end());
+  for (size_t i = 1; i < rows.size(); ++i)
+    if (rows[i - 1].second > rows[i].first)
+      return fail(WF_ERR_INVALID, "query row ranges of two groups overlap at row %d",
+                  rows[i].first);
+  if (lse && (lse_stride < max_row || lse_stride > 0x7fffffff))
+    return fail(WF_ERR_INVALID, "lse_stride %lld must cover row %lld and fit 32 bits",
+                (long long)lse_stride, (long long)max_row);
+  if (any_rows) {
+    if ((rc = check_rows("q", q, q_row_stride, pool))) return rc;
+    if ((rc = check_rows("out", out, out_row_stride, pool))) return rc;
+  }
+  return launch_groups(pool, specs, q, q_row_stride, scale, out, out_row_stride, lse,
+                       lse ? lse_stride : 0, stream);
 }
 
 }  // extern "C"

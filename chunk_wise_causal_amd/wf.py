@@ -41,6 +41,15 @@ class wf_rope(ctypes.Structure):
                 ("theta", ctypes.c_double)]
 
 
+class wf_kv_run(ctypes.Structure):
+    _fields_ = [("kv_start", ctypes.c_int32), ("kv_len", ctypes.c_int32)]
+
+
+class wf_query_group(ctypes.Structure):
+    _fields_ = [("q_row_start", ctypes.c_int32), ("q_row_end", ctypes.c_int32),
+                ("run_begin", ctypes.c_int32), ("run_end", ctypes.c_int32)]
+
+
 class wf_segment(ctypes.Structure):
     _fields_ = [("kv_start", ctypes.c_int32), ("kv_len", ctypes.c_int32),
                 ("slot", ctypes.c_int32)]
@@ -65,6 +74,10 @@ def lib() -> ctypes.CDLL:
                                     vp, i64, ctypes.POINTER(i32), i32, i32, ctypes.c_float,
                                     vp, i64, vp, vp]
         L.wf_chunk_attn.restype = ctypes.c_int
+        L.wf_group_attn.argtypes = [ctypes.POINTER(wf_kv_pool), ctypes.POINTER(wf_kv_run), i32,
+                                    ctypes.POINTER(wf_query_group), i32, vp, i64, ctypes.c_float,
+                                    vp, i64, vp, i64, vp]
+        L.wf_group_attn.restype = ctypes.c_int
         L.wf_last_error.restype = ctypes.c_char_p
         L.wf_last_error.argtypes = []
         L.wf_version.restype = ctypes.c_char_p
@@ -167,6 +180,32 @@ def wf_chunk_attn(pool: KVPool, segments: Sequence[Tuple[int, int, int]], q: tor
                              _row_stride(q, "q"), qss, len(q_slot_start) - 1, first_slot,
                              float(scale), _ptr(out), _row_stride(out, "out"), _ptr(lse),
                              _stream(stream))
+    _check(rc)
+    return out
+
+
+def wf_group_attn(pool: KVPool, runs: Sequence[Tuple[int, int]],
+                  groups: Sequence[Tuple[int, int, int, int]], q: torch.Tensor,
+                  scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                  lse: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Attention of arbitrary query groups over the pool (C: wf_group_attn).
+    runs: (kv_start, kv_len); groups: (q_row_start, q_row_end, run_begin,
+    run_end).  lse, if given, is [H, n] float32 with n >= every q_row_end.
+    Returns `out` ([rows, H, D], allocated if None)."""
+    if out is None:
+        out = torch.empty_like(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    rs = (wf_kv_run * len(runs))(*[wf_kv_run(*r) for r in runs])
+    gs = (wf_query_group * len(groups))(*[wf_query_group(*g) for g in groups])
+    lse_stride = 0
+    if lse is not None:
+        if lse.dim() != 2 or lse.dtype != torch.float32 or lse.stride(1) != 1:
+            raise ValueError("lse: expected [heads, n] float32 with contiguous rows")
+        lse_stride = lse.stride(0)
+    rc = lib().wf_group_attn(ctypes.byref(pool.desc), rs, len(runs), gs, len(groups), _ptr(q),
+                             _row_stride(q, "q"), float(scale), _ptr(out),
+                             _row_stride(out, "out"), _ptr(lse), lse_stride, _stream(stream))
     _check(rc)
     return out
 

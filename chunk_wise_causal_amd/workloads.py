@@ -33,7 +33,7 @@ from typing import List, Optional, Tuple
 import numpy as np
 import torch
 
-__all__ = ["Config", "CONFIGS", "Workload", "make_workload", "small_config"]
+__all__ = ["Config", "CONFIGS", "Workload", "make_workload", "small_config", "query_groups"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -259,3 +259,33 @@ def bf16_bits(t: torch.Tensor) -> np.ndarray:
     """uint16 bit patterns of a bfloat16 tensor (no arithmetic)."""
     assert t.dtype == torch.bfloat16
     return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def query_groups(cfg: Config, seed: int = 0):
+    """A seeded layout of query groups for the generic entry point, as
+    (runs, groups) with runs (kv_start, kv_len) and groups (q_row_start,
+    q_row_end, run_begin, run_end), over the cfg.n_q query rows:
+
+      rows [0, C)       the store stage: the first chunk of rows stands in for
+                        the store chunk's queries, over anchor | history |
+                        store = [0, cfg.prefix)
+      rows [C, 2C)      three random disjoint runs of random (unaligned)
+                        lengths anywhere in [0, n_kv), listed out of order
+      rows [2C, n_q)    (if any) the whole context, given as one run per
+                        segment, so adjacent runs must be merged
+    """
+    rng = np.random.Generator(np.random.PCG64(10_000 + seed))
+    C, n_kv = cfg.chunk, cfg.n_kv
+    runs = [(0, cfg.prefix)]
+    groups = [(0, C, 0, 1)]
+    cuts = np.sort(rng.choice(np.arange(1, n_kv), size=5, replace=False))
+    rnd = [(int(cuts[0]), int(cuts[1] - cuts[0])), (int(cuts[2]), int(cuts[3] - cuts[2])),
+           (int(cuts[4]), int(n_kv - cuts[4]))]
+    rnd = [rnd[i] for i in rng.permutation(3)]
+    groups.append((C, min(2 * C, cfg.n_q), len(runs), len(runs) + 3))
+    runs += rnd
+    if cfg.n_q > 2 * C:
+        segs = [(st, ln) for (st, ln, _) in cfg.segments()]
+        groups.append((2 * C, cfg.n_q, len(runs), len(runs) + len(segs)))
+        runs += segs
+    return runs, groups

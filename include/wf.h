@@ -216,6 +216,63 @@ int wf_chunk_attn(const wf_kv_pool* pool,
                   void* out, int64_t out_row_stride,
                   float* lse, hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * wf_group_attn — attention forward for arbitrary query groups over the pool.
+ *
+ * The same computation as wf_chunk_attn with the visibility given per group
+ * instead of derived from slots.  It covers the store stage ("Wave Forcing:
+ * Towards Speed-of-Light Streaming Video Generation", overview and §B.1:
+ * the store stage runs on its own replica; §3.1: its chunk sits after the
+ * anchor and the clean history in the per-layer context), whose queries are
+ * the store chunk over anchor | history | store, and any layout where a
+ * group's keys are not a slot rule (rotated history, gaps).
+ *
+ * For every head h, group g and query row i in [q_row_start, q_row_end) of
+ * g, with vis(g) the union of the runs runs[run_begin .. run_end):
+ *   z_L   = scale * <q[i][h], K_L[h]>                    for L in vis(g)
+ *   out[i][h] = sum_L softmax(z)_L * V_L[h]
+ *   lse[h * lse_stride + i] = log(sum_L exp(z_L))   (natural log, if lse)
+ * Attention inside vis(g) is full; keys outside it are never read.
+ *
+ *   pool           host struct; pages as written by wf_kv_publish
+ *   runs, n_runs   host array, 1 <= n_runs <= 256; each run inside
+ *                  [0, num_logical_pages * page_size), kv_len >= 1
+ *   groups         host array, 1 <= n_groups <= 32; 0 <= q_row_start <=
+ *                  q_row_end; 0 <= run_begin < run_end <= n_runs; the runs
+ *                  of one group must not overlap (different groups may share
+ *                  keys); the row ranges of different groups must not overlap
+ *   q              device, query rows of [num_heads][head_dim], RoPE applied
+ *   q_row_stride   elements between query rows
+ *   scale          softmax scale, finite and > 0
+ *   out            device, same row layout as q; written for every row of
+ *                  every group, nothing else
+ *   out_row_stride elements between output rows
+ *   lse            device float [num_heads][lse_stride], nullable
+ *   lse_stride     >= the largest q_row_end (ignored if lse == NULL)
+ * After merging adjacent runs, the visible ranges of all groups together
+ * must number at most 256 (else WF_ERR_UNSUPPORTED).
+ * Aliasing: out must not overlap q, lse or the pool.
+ * Returns WF_OK, WF_ERR_INVALID, WF_ERR_UNSUPPORTED or WF_ERR_HIP.
+ */
+typedef struct {
+  int32_t kv_start;  /* first logical token of the run */
+  int32_t kv_len;    /* tokens in the run, >= 1 */
+} wf_kv_run;
+
+typedef struct {
+  int32_t q_row_start;  /* query rows [q_row_start, q_row_end) */
+  int32_t q_row_end;
+  int32_t run_begin;    /* visible keys: runs[run_begin .. run_end) */
+  int32_t run_end;
+} wf_query_group;
+
+int wf_group_attn(const wf_kv_pool* pool,
+                  const wf_kv_run* runs, int32_t n_runs,
+                  const wf_query_group* groups, int32_t n_groups,
+                  const void* q, int64_t q_row_stride, float scale,
+                  void* out, int64_t out_row_stride,
+                  float* lse, int64_t lse_stride, hipStream_t stream);
+
 /* Message describing the last failure of a wf_* call on this thread ("" if
  * the last call succeeded).  The string is owned by the library. */
 const char* wf_last_error(void);

@@ -82,6 +82,46 @@ def chunk_attention(k_pool, v_pool, page_table, page_size: int, segments,
     return out, lse
 
 
+def run_tokens(runs) -> np.ndarray:
+    """Sorted logical tokens of a union of (kv_start, kv_len) runs."""
+    parts = [np.arange(st, st + ln, dtype=np.int64) for (st, ln) in runs]
+    if not parts:
+        return np.zeros(0, dtype=np.int64)
+    return np.sort(np.concatenate(parts))
+
+
+def group_attention(k_pool, v_pool, page_table, page_size: int, runs, groups,
+                    q: np.ndarray, scale: float, dtype: str,
+                    heads: Optional[Iterable[int]] = None, block: int = 1024):
+    """Attention of arbitrary query groups: group (r0, r1, b, e) is rows
+    [r0, r1) attending, fully, to the union of runs[b:e].  The store stage
+    ([WF] overview and §B.1; §3.1 context order) is the group of the store
+    chunk's rows over anchor | history | store.  Same definition as
+    chunk_attention with the visible set given per group.  Returns (out,
+    lse) as float64 [n_rows, H, D] and [H, n_rows]; rows outside every group
+    are NaN."""
+    n_rows, H, D = q.shape
+    heads = range(H) if heads is None else list(heads)
+    out = np.full((n_rows, H, D), np.nan)
+    lse = np.full((H, n_rows), np.nan)
+    for (r0, r1, b, e) in groups:
+        if r1 <= r0:
+            continue
+        vis = run_tokens(runs[b:e])
+        for h in heads:
+            kh, vh = gather(k_pool[:, h:h + 1], v_pool[:, h:h + 1], page_table,
+                            page_size, vis)
+            kh = to_f32(kh[:, 0], dtype).astype(np.float64)
+            vh = to_f32(vh[:, 0], dtype).astype(np.float64)
+            for i in range(r0, r1, block):
+                idx = np.arange(i, min(r1, i + block))
+                qh = to_f32(q[idx, h], dtype).astype(np.float64)
+                o, l = _softmax_attend(qh, kh, vh, scale)
+                out[idx, h] = o
+                lse[h, idx] = l
+    return out, lse
+
+
 def probabilities(k_pool, v_pool, page_table, page_size: int, segments,
                   q_rows: np.ndarray, s: int, h: int, scale: float, dtype: str):
     """Softmax weights [n, |vis(s)|] of the given query rows (storage

@@ -43,3 +43,33 @@ def brute_attention(q: np.ndarray, k_logical: np.ndarray, v_logical: np.ndarray,
                 out[i, h] = acc / l
                 lse[h, i] = m + math.log(l)
     return out, lse
+
+
+def brute_group_attention(q: np.ndarray, k_logical: np.ndarray, v_logical: np.ndarray,
+                          runs, groups, scale: float):
+    """Query groups with explicit key runs, the slow way: for each row of
+    group (r0, r1, b, e), every logical token L is tested on its own for
+    membership in one of runs[b:e].  float64 in, out [n_rows, H, D] and
+    lse [H, n_rows] out (NaN outside every group)."""
+    n_rows, H, D = q.shape
+    n_kv = k_logical.shape[0]
+    out = np.full((n_rows, H, D), np.nan)
+    lse = np.full((H, n_rows), np.nan)
+    for (r0, r1, b, e) in groups:
+        for h in range(H):
+            for i in range(r0, r1):
+                scores, values = [], []
+                for L in range(n_kv):
+                    if not any(st <= L < st + ln for (st, ln) in runs[b:e]):
+                        continue
+                    scores.append(scale * float(np.dot(q[i, h], k_logical[L, h])))
+                    values.append(v_logical[L, h])
+                m = max(scores)
+                w = [math.exp(z - m) for z in scores]
+                l = math.fsum(w)
+                acc = np.zeros(D)
+                for wi, vi in zip(w, values):
+                    acc += wi * vi
+                out[i, h] = acc / l
+                lse[h, i] = m + math.log(l)
+    return out, lse

@@ -160,3 +160,53 @@ def test_binding_raises_with_message(L):
     with pytest.raises(wf.WFError, match="page_size"):
         wf.wf_chunk_attn(p, [(0, 10, 0)], torch.empty(4, 4, 128), [0, 4], out=torch.empty(4, 4, 128),
                          stream=0)
+
+
+def gattn(L, p=None, runs=((0, 100), (100, 50), (150, 50)),
+          groups=((0, 50, 0, 3), (50, 100, 0, 2)), q=FAKE, qs=512, scale=0.088, out=FAKE,
+          os_=512, lse=None, lse_stride=0, n_runs=None, n_groups=None):
+    p = p or pool()
+    ra = (wf.wf_kv_run * max(1, len(runs)))(*[wf.wf_kv_run(*r) for r in runs])
+    ga = (wf.wf_query_group * max(1, len(groups)))(*[wf.wf_query_group(*g) for g in groups])
+    rc = L.wf_group_attn(ctypes.byref(p), ra, len(runs) if n_runs is None else n_runs, ga,
+                         len(groups) if n_groups is None else n_groups, q, qs, scale, out, os_,
+                         lse, lse_stride, None)
+    return rc, L.wf_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(runs=((0, 100), (90, 50), (150, 50))), wf.WF_ERR_INVALID, "overlap"),
+    (dict(runs=((0, 100), (100, 0), (150, 50))), wf.WF_ERR_INVALID, "outside"),
+    (dict(runs=((0, 100), (100, 50), (2550, 50))), wf.WF_ERR_INVALID, "outside"),
+    (dict(runs=((-1, 100), (100, 50), (150, 50))), wf.WF_ERR_INVALID, "outside"),
+    (dict(n_runs=0), wf.WF_ERR_INVALID, "n_runs"),
+    (dict(n_runs=257), wf.WF_ERR_INVALID, "n_runs"),
+    (dict(n_groups=0), wf.WF_ERR_INVALID, "n_groups"),
+    (dict(n_groups=33), wf.WF_ERR_INVALID, "n_groups"),
+    (dict(groups=((0, 50, 0, 3), (40, 100, 0, 2))), wf.WF_ERR_INVALID, "overlap at row 40"),
+    (dict(groups=((0, 50, 2, 2),)), wf.WF_ERR_INVALID, "runs"),
+    (dict(groups=((0, 50, 1, 4),)), wf.WF_ERR_INVALID, "runs"),
+    (dict(groups=((-1, 50, 0, 1),)), wf.WF_ERR_INVALID, "rows"),
+    (dict(groups=((60, 50, 0, 1),)), wf.WF_ERR_INVALID, "rows"),
+    (dict(scale=-1.0), wf.WF_ERR_INVALID, "scale"),
+    (dict(q=None), wf.WF_ERR_INVALID, "q is NULL"),
+    (dict(os_=256), wf.WF_ERR_INVALID, "out_row_stride"),
+    (dict(lse=FAKE, lse_stride=99), wf.WF_ERR_INVALID, "lse_stride"),
+])
+def test_group_attn_rejects(L, kw, code, msg):
+    rc, err = gattn(L, **kw)
+    assert rc == code, err
+    assert msg in err
+
+
+def test_group_attn_shared_keys_and_noop(L):
+    # groups may share runs; rows may be empty; no rows at all is a no-op
+    rc, err = gattn(L, groups=((0, 0, 0, 3), (5, 5, 1, 2)), q=None, out=None)
+    assert rc == wf.WF_OK and err == ""
+
+
+def test_group_attn_too_many_ranges_unsupported(L):
+    runs = [(i * 20, 10) for i in range(120)]
+    groups = [(g, g + 1, 0, 120) for g in range(3)]   # 3 x 120 unmergeable ranges
+    rc, err = gattn(L, runs=runs, groups=groups)
+    assert rc == wf.WF_ERR_UNSUPPORTED and "ranges" in err

@@ -209,3 +209,67 @@ def test_hot_rows_config_draws():
     assert len(wl.hot_rows) == round(0.05 * cfg.n_kv)
     big = np.abs(wl.k.float().numpy()).max(axis=(1, 2))
     assert big[wl.hot_rows].mean() > 4 * np.delete(big, wl.hot_rows).mean()
+
+
+# ---- generic query groups (store stage, explicit key runs) -----------------
+
+from chunk_wise_causal_amd.workloads import query_groups
+from oracle.attention import group_attention, run_tokens
+from oracle.brute import brute_group_attention
+
+
+def _gattn(wl, ref, runs, groups):
+    c = wl.cfg
+    return group_attention(ref["k_pool"], ref["v_pool"], wl.page_table, c.page_size, runs,
+                           groups, ref["q"], c.scale, c.dtype)
+
+
+@pytest.mark.parametrize("cfg", [CONFIGS[1], small_config(slots=2)], ids=["cfg1_fp32", "small_bf16"])
+def test_group_attention_matches_brute_force(cfg):
+    wl = make_workload(cfg)
+    ref = oracle_layer(wl)
+    c = wl.cfg
+    runs, groups = query_groups(c, seed=1)
+    out, lse = _gattn(wl, ref, runs, groups)
+    bo, bl = brute_group_attention(f64(ref["q"], c.dtype), f64(ref["k_rot"], c.dtype),
+                                   f64(ref["v"], c.dtype), runs, groups, c.scale)
+    np.testing.assert_allclose(out, bo, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, bl, rtol=0, atol=1e-12)
+
+
+def test_store_stage_is_dense_attention_over_the_prefix():
+    """The store chunk's queries see anchor | history | store: dense
+    attention (torch fp64 SDPA on CPU) over exactly those keys."""
+    wl = make_workload(small_config())
+    ref = oracle_layer(wl)
+    c = wl.cfg
+    runs, groups = [(0, c.prefix)], [(0, c.chunk, 0, 1)]
+    out, lse = _gattn(wl, ref, runs, groups)
+    q = torch.from_numpy(f64(ref["q"], c.dtype)[:c.chunk]).permute(1, 0, 2)
+    k = torch.from_numpy(f64(ref["k_rot"], c.dtype)[:c.prefix]).permute(1, 0, 2).contiguous()
+    v = torch.from_numpy(f64(ref["v"], c.dtype)[:c.prefix]).permute(1, 0, 2).contiguous()
+    o_ref = torch.nn.functional.scaled_dot_product_attention(q, k, v, scale=c.scale)
+    np.testing.assert_allclose(out[:c.chunk], o_ref.permute(1, 0, 2).numpy(), rtol=0, atol=1e-12)
+    assert np.isnan(out[c.chunk:]).all() and np.isnan(lse[:, c.chunk:]).all()
+
+
+def test_slot_rule_as_groups_reproduces_chunk_attention():
+    """wf_chunk_attn's visibility written out as explicit runs per slot
+    gives the same numbers through the group definition."""
+    wl = make_workload(small_config())
+    ref = oracle_layer(wl)
+    c = wl.cfg
+    runs, groups = [], []
+    qss = c.q_slot_start()
+    for s in range(c.slots):
+        mine = [(st, ln) for (st, ln, sl) in c.segments() if sl < 0 or sl >= s]
+        groups.append((qss[s], qss[s + 1], len(runs), len(runs) + len(mine)))
+        runs += mine
+    out, lse = _gattn(wl, ref, runs, groups)
+    o2, l2 = _attn(wl, ref)
+    np.testing.assert_array_equal(out, o2)
+    np.testing.assert_array_equal(lse, l2)
+
+
+def test_run_tokens_is_the_union():
+    assert list(run_tokens([(5, 2), (0, 3)])) == [0, 1, 2, 5, 6]
