@@ -33,7 +33,8 @@ from typing import List, Optional, Tuple
 import numpy as np
 import torch
 
-__all__ = ["Config", "CONFIGS", "Workload", "make_workload", "small_config", "query_groups"]
+__all__ = ["Config", "CONFIGS", "Workload", "make_workload", "small_config", "query_groups",
+           "AlignedLayout", "initial_context", "round_inputs"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -289,3 +290,109 @@ def query_groups(cfg: Config, seed: int = 0):
         groups.append((2 * C, cfg.n_q, len(runs), len(runs) + len(segs)))
         runs += segs
     return runs, groups
+
+
+@dataclasses.dataclass(frozen=True)
+class AlignedLayout:
+    """The same context on page boundaries, for rotating the history by
+    page-table edits: the anchor and every chunk start on a page, a chunk of
+    C tokens occupies ceil(C / page_size) pages, and the tail of its last page
+    is a gap no segment names.  Logical order is unchanged:
+
+        anchor | history 0 (oldest) .. | store | slot 0 | .. | slot W-1
+
+    The rotation window is history + store: n_hist + 1 chunks from
+    window_start, chunk_stride tokens each.
+    """
+    cfg: Config
+
+    @property
+    def chunk_stride(self) -> int:
+        ps = self.cfg.page_size
+        return -(-self.cfg.chunk // ps) * ps
+
+    @property
+    def window_start(self) -> int:
+        ps = self.cfg.page_size
+        return -(-self.cfg.anchor_tokens // ps) * ps
+
+    @property
+    def window_chunks(self) -> int:
+        return self.cfg.n_hist + 1
+
+    def hist_start(self, k: int) -> int:
+        return self.window_start + k * self.chunk_stride
+
+    @property
+    def store_start(self) -> int:
+        return self.hist_start(self.cfg.n_hist)
+
+    def slot_start(self, j: int) -> int:
+        return self.store_start + (j + 1) * self.chunk_stride
+
+    @property
+    def span(self) -> int:
+        """Logical tokens covered, gaps included (a whole number of pages)."""
+        return self.slot_start(self.cfg.slots)
+
+    @property
+    def n_logical_pages(self) -> int:
+        return self.span // self.cfg.page_size
+
+    def segments(self) -> List[Tuple[int, int, int]]:
+        c = self.cfg
+        segs = [(0, c.anchor_tokens, -1)] if c.anchor_tokens else []
+        segs += [(self.hist_start(k), c.chunk, -1) for k in range(c.n_hist)]
+        segs.append((self.store_start, c.chunk, -1))
+        segs += [(self.slot_start(j), c.chunk, j) for j in range(c.slots)]
+        return segs
+
+
+def round_inputs(cfg: Config, rnd: int, seed: int = 0):
+    """Fresh inputs of streaming round `rnd` (seeded per round): K and V of
+    the store chunk and the W slot chunks ([W+1, C, H, D], store first, then
+    slot 0..W-1), the slot queries [W*C, H, D] and (t, h, w) positions
+    [W+1, C, 3].  In round r the store holds latent frames after the r
+    chunks completed before it (history starts at frame 1, after the anchor's
+    frame 0); slot W-1 is the next chunk and slot 0 the newest."""
+    g = torch.Generator().manual_seed(1_000_003 * (seed + 1) + rnd)
+    H, D, C, W = cfg.heads, cfg.head_dim, cfg.chunk, cfg.slots
+    td = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    k = torch.randn(W + 1, C, H, D, generator=g).to(td)
+    v = torch.randn(W + 1, C, H, D, generator=g).to(td)
+    q = torch.randn(W * C, H, D, generator=g).to(td)
+    hw = cfg.frame_rows * cfg.frame_cols
+    tok = np.arange(C, dtype=np.int32)
+    fpc = cfg.frames_per_chunk
+    store_frame = 1 + (cfg.n_hist + rnd) * fpc
+    pos = np.empty((W + 1, C, 3), dtype=np.int32)
+    for c in range(W + 1):
+        # c = 0: store; c = 1 + j: slot j, whose frame is store + (W - j) chunks
+        f0 = store_frame + (0 if c == 0 else (W - (c - 1)) * fpc)
+        pos[c, :, 0] = f0 + tok // hw
+        pos[c, :, 1] = (tok % hw) // cfg.frame_cols
+        pos[c, :, 2] = (tok % hw) % cfg.frame_cols
+    return k, v, q, pos
+
+
+def initial_context(cfg: Config, seed: int = 0):
+    """The context resident before round 0: anchor K, V [A, H, D] with
+    positions [A, 3] (frame 0), and the history chunks K, V [n_hist, C, H, D]
+    with positions [n_hist, C, 3] (frames 1.., oldest first)."""
+    g = torch.Generator().manual_seed(7_000_001 * (seed + 1))
+    H, D, C, A = cfg.heads, cfg.head_dim, cfg.chunk, cfg.anchor_tokens
+    td = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    ka = torch.randn(A, H, D, generator=g).to(td)
+    va = torch.randn(A, H, D, generator=g).to(td)
+    kh = torch.randn(cfg.n_hist, C, H, D, generator=g).to(td)
+    vh = torch.randn(cfg.n_hist, C, H, D, generator=g).to(td)
+    hw = cfg.frame_rows * cfg.frame_cols
+    ta = np.arange(A, dtype=np.int32) % hw
+    pa = np.stack([np.zeros(A, np.int32), ta // cfg.frame_cols, ta % cfg.frame_cols], axis=1)
+    tok = np.arange(C, dtype=np.int32)
+    ph = np.empty((cfg.n_hist, C, 3), dtype=np.int32)
+    for k in range(cfg.n_hist):
+        ph[k, :, 0] = 1 + k * cfg.frames_per_chunk + tok // hw
+        ph[k, :, 1] = (tok % hw) // cfg.frame_cols
+        ph[k, :, 2] = (tok % hw) % cfg.frame_cols
+    return (ka, va, pa), (kh, vh, ph)

@@ -20,6 +20,7 @@ Modules:
   publish    paged scatter of K/V into the pool through the page table
   attention  masked softmax attention per query slot, float64
   brute      the same attention with explicit per-key loops (tiny inputs)
+  history    end-of-round history rotation as a page-table reordering
 
 Parity status: every function here is pinned by tests/test_oracle_*.py
 against closed forms, textbook/library special cases, invariants the pages
