@@ -16,7 +16,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libwf.so")
-SOURCES = ["api.cpp", "status.hip", "publish.hip", "attn_bf16.hip", "attn_fp32.hip"]
+SOURCES = ["api.cpp", "status.hip", "publish.hip", "attn_bf16.hip", "attn_fp32.hip",
+           "rotate.hip"]
 ARCH = "gfx950"
 
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

@@ -408,4 +408,37 @@ int wf_group_attn(const wf_kv_pool* pool, const wf_kv_run* runs, int32_t n_runs,
                        lse ? lse_stride : 0, stream);
 }
 
+// History rotation ([WF] §3.1, bounded clean history then live store): the
+// window's table entries rotate left by one chunk; pages do not move.
+int wf_history_rotate(int32_t* page_table, int32_t num_logical_pages, int32_t page_size,
+                      int32_t window_start, int32_t chunk_stride, int32_t n_chunks,
+                      hipStream_t stream) {
+  if (!page_table) return fail(WF_ERR_INVALID, "page_table is NULL");
+  if ((reinterpret_cast<uintptr_t>(page_table) & 3u) != 0)
+    return fail(WF_ERR_INVALID, "page_table must be 4-byte aligned");
+  if (num_logical_pages < 1) return fail(WF_ERR_INVALID, "num_logical_pages must be >= 1");
+  if (page_size < 16 || page_size > 1024 || log2_exact(page_size) < 0)
+    return fail(WF_ERR_INVALID, "page_size %d is not a power of two in [16, 1024]", page_size);
+  if (window_start < 0 || window_start % page_size != 0)
+    return fail(WF_ERR_INVALID, "window_start %d is not a non-negative multiple of page_size",
+                window_start);
+  if (chunk_stride < page_size || chunk_stride % page_size != 0)
+    return fail(WF_ERR_INVALID, "chunk_stride %d is not a positive multiple of page_size",
+                chunk_stride);
+  if (n_chunks < 1) return fail(WF_ERR_INVALID, "n_chunks must be >= 1");
+  const int64_t first = window_start / page_size;
+  const int64_t cp = chunk_stride / page_size;
+  const int64_t n = cp * n_chunks;
+  if (first + n > num_logical_pages)
+    return fail(WF_ERR_INVALID, "window [%lld, %lld) pages exceeds num_logical_pages %d",
+                (long long)first, (long long)(first + n), num_logical_pages);
+  if (n > wf::kMaxRotatePages)
+    return fail(WF_ERR_UNSUPPORTED, "window of %lld pages exceeds the limit of %d",
+                (long long)n, wf::kMaxRotatePages);
+  if (n_chunks == 1) return ok();
+  const hipError_t e = wf::launch_rotate(page_table, (int)first, (int)n, (int)cp, stream);
+  if (e != hipSuccess) return hip_fail(e, "rotation launch");
+  return ok();
+}
+
 }  // extern "C"

@@ -78,6 +78,8 @@ def lib() -> ctypes.CDLL:
                                     ctypes.POINTER(wf_query_group), i32, vp, i64, ctypes.c_float,
                                     vp, i64, vp, i64, vp]
         L.wf_group_attn.restype = ctypes.c_int
+        L.wf_history_rotate.argtypes = [vp, i32, i32, i32, i32, i32, vp]
+        L.wf_history_rotate.restype = ctypes.c_int
         L.wf_last_error.restype = ctypes.c_char_p
         L.wf_last_error.argtypes = []
         L.wf_version.restype = ctypes.c_char_p
@@ -208,6 +210,17 @@ def wf_group_attn(pool: KVPool, runs: Sequence[Tuple[int, int]],
                              _row_stride(out, "out"), _ptr(lse), lse_stride, _stream(stream))
     _check(rc)
     return out
+
+
+def wf_history_rotate(pool: KVPool, window_start: int, chunk_stride: int, n_chunks: int,
+                      stream=None) -> None:
+    """End-of-round history rotation (C: wf_history_rotate): the pool's page
+    table entries of the window [window_start, window_start + n_chunks *
+    chunk_stride) rotate left by one chunk, in place; no page moves."""
+    t = pool.page_table
+    rc = lib().wf_history_rotate(_ptr(t), t.numel(), pool.page_size, window_start,
+                                 chunk_stride, n_chunks, _stream(stream))
+    _check(rc)
 
 
 def wf_device_status(clear: bool = True) -> int:

@@ -273,6 +273,44 @@ int wf_group_attn(const wf_kv_pool* pool,
                   void* out, int64_t out_row_stride,
                   float* lse, int64_t lse_stride, hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * wf_history_rotate — end-of-round history rotation by page-table edits
+ * ([WF] §3.1: the context holds a bounded clean history, oldest first,
+ * followed by the live store; when a round completes a chunk, the store joins
+ * the history as its newest chunk and the oldest history chunk leaves).
+ *
+ * The window of logical tokens [window_start, window_start + n_chunks *
+ * chunk_stride) holds n_chunks chunks of chunk_stride tokens each: the
+ * history chunks, oldest first, then the live store.  The call rotates the
+ * window's page-table entries left by one chunk, in place:
+ *   new[w0 + i] = old[w0 + (i + cp) mod n]     for i in [0, n)
+ * with w0 = window_start / page_size, cp = chunk_stride / page_size and
+ * n = n_chunks * cp.  Afterwards the history reads, oldest first, the old
+ * history without its oldest chunk and then the old store; the store position
+ * maps to the evicted chunk's physical pages, which the next round's
+ * wf_kv_publish of the store overwrites.  No K/V byte moves and no other
+ * entry changes.  Copy-free rotation needs chunks that start on page
+ * boundaries: window_start and chunk_stride must be multiples of page_size
+ * (a chunk of C tokens then occupies ceil(C / page_size) pages; the tail of
+ * its last page is a gap that no segment names).
+ *
+ *   page_table       device int32 [num_logical_pages] (the pool's table),
+ *                    updated in place; its entries are moved, never read
+ *                    as page numbers
+ *   num_logical_pages, page_size   as in the pool
+ *   window_start     >= 0, multiple of page_size
+ *   chunk_stride     >= page_size, multiple of page_size
+ *   n_chunks         >= 1 (1 is a no-op); the window must end at or before
+ *                    num_logical_pages * page_size and span at most 16384
+ *                    pages (else WF_ERR_UNSUPPORTED)
+ * Stream-ordered like every call: attention or publish work enqueued earlier
+ * on the stream sees the old table, later work the new one.
+ * Returns WF_OK, WF_ERR_INVALID, WF_ERR_UNSUPPORTED or WF_ERR_HIP.
+ */
+int wf_history_rotate(int32_t* page_table, int32_t num_logical_pages, int32_t page_size,
+                      int32_t window_start, int32_t chunk_stride, int32_t n_chunks,
+                      hipStream_t stream);
+
 /* Message describing the last failure of a wf_* call on this thread ("" if
  * the last call succeeded).  The string is owned by the library. */
 const char* wf_last_error(void);

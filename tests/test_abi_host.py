@@ -210,3 +210,34 @@ def test_group_attn_too_many_ranges_unsupported(L):
     groups = [(g, g + 1, 0, 120) for g in range(3)]   # 3 x 120 unmergeable ranges
     rc, err = gattn(L, runs=runs, groups=groups)
     assert rc == wf.WF_ERR_UNSUPPORTED and "ranges" in err
+
+
+def rotate(L, table=FAKE, nlp=64, ps=256, start=512, stride=1024, n=3):
+    rc = L.wf_history_rotate(table, nlp, ps, start, stride, n, None)
+    return rc, L.wf_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(table=None), wf.WF_ERR_INVALID, "NULL"),
+    (dict(table=FAKE + 2), wf.WF_ERR_INVALID, "aligned"),
+    (dict(nlp=0), wf.WF_ERR_INVALID, "num_logical_pages"),
+    (dict(ps=100), wf.WF_ERR_INVALID, "page_size"),
+    (dict(ps=8), wf.WF_ERR_INVALID, "page_size"),
+    (dict(start=-256), wf.WF_ERR_INVALID, "window_start"),
+    (dict(start=100), wf.WF_ERR_INVALID, "window_start"),
+    (dict(stride=0), wf.WF_ERR_INVALID, "chunk_stride"),
+    (dict(stride=1000), wf.WF_ERR_INVALID, "chunk_stride"),
+    (dict(n=0), wf.WF_ERR_INVALID, "n_chunks"),
+    (dict(nlp=13), wf.WF_ERR_INVALID, "exceeds num_logical_pages"),   # window ends at page 14
+    (dict(nlp=1 << 20, ps=16, start=0, stride=16, n=16385), wf.WF_ERR_UNSUPPORTED, "limit"),
+])
+def test_history_rotate_rejects(L, kw, code, msg):
+    rc, err = rotate(L, **kw)
+    assert rc == code and msg in err, (rc, err)
+
+
+def test_history_rotate_single_chunk_is_noop(L):
+    # one chunk: rotating by the whole window is the identity, nothing is launched
+    assert rotate(L, n=1) == (wf.WF_OK, "")
+    # the window may end exactly at the table's end
+    assert rotate(L, nlp=14, n=1)[0] == wf.WF_OK
