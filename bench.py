@@ -156,6 +156,35 @@ def cpu_baseline(cfg, seconds: float):
     }
 
 
+def time_history_rotate(cfg, torch, wf, reps: int = 200):
+    """End-of-round history rotation (wf_history_rotate) on the page-aligned
+    placement of the same context: average launch duration over `reps`
+    rotations, HIP events on the launch stream."""
+    from chunk_wise_causal_amd.workloads import AlignedLayout
+    lay = AlignedLayout(cfg)
+    table = torch.randperm(lay.n_logical_pages, dtype=torch.int32, device="cuda")
+    pool = wf.KVPool(torch.empty(1, 1, cfg.page_size, cfg.head_dim, dtype=torch.bfloat16,
+                                 device="cuda"),
+                     torch.empty(1, 1, cfg.head_dim, cfg.page_size, dtype=torch.bfloat16,
+                                 device="cuda"), table)
+    stream = torch.cuda.current_stream()
+    for _ in range(10):
+        wf.wf_history_rotate(pool, lay.window_start, lay.chunk_stride, lay.window_chunks,
+                             stream=stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        wf.wf_history_rotate(pool, lay.window_start, lay.chunk_stride, lay.window_chunks,
+                             stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    window = lay.window_chunks * lay.chunk_stride // cfg.page_size
+    return {"us_per_rotation": round(e0.elapsed_time(e1) * 1e3 / reps, 3),
+            "window_pages": window, "table_pages": lay.n_logical_pages,
+            "chunk_pages": lay.chunk_stride // cfg.page_size,
+            "layout": "page-aligned placement of the same context"}
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -245,6 +274,7 @@ def main():
                      "kernel": "attn_fwd_bf16<128, true>"},
         "cpu_baseline": None,
     }
+    res["history_rotate"] = time_history_rotate(cfg, torch, wf)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
     print(json.dumps(res), flush=True)

@@ -16,6 +16,7 @@
 
 #include "../../include/wf.h"
 #include "wf_internal.h"
+#include "wf_rotate.h"
 
 namespace {
 

@@ -12,7 +12,7 @@
 // few chunks of tens of pages), so one workgroup reads all of it into LDS,
 // then writes it back rotated: every read precedes every write, which makes
 // the in-place update safe without a second buffer.
-#include "wf_internal.h"
+#include "wf_rotate.h"
 
 namespace wf {
 namespace {

@@ -65,10 +65,6 @@ hipError_t launch_attn_bf16(const AttnParams& p, int head_dim, int block_m,
                             hipStream_t stream);
 hipError_t launch_attn_fp32(const AttnParams& p, int head_dim, int block_m,
                             hipStream_t stream);
-// window of n table entries from `first`, rotated left by `shift` (0 <= shift
-// < n <= kMaxRotatePages)
-constexpr int kMaxRotatePages = 16384;
-hipError_t launch_rotate(int32_t* table, int first, int n, int shift, hipStream_t stream);
 
 // per-device status word (status.hip)
 int* status_word_ptr(hipError_t* err);
