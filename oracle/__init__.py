@@ -21,6 +21,8 @@ Modules:
   attention  masked softmax attention per query slot, float64
   brute      the same attention with explicit per-key loops (tiny inputs)
   history    end-of-round history rotation as a page-table reordering
+  mx         MXFP8 (E4M3 + E8M0 block scale) keys and queries for the
+             8-bit QK^T variant, and its attention
 
 Parity status: every function here is pinned by tests/test_oracle_*.py
 against closed forms, textbook/library special cases, invariants the pages
