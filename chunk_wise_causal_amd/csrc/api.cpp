@@ -16,6 +16,7 @@
 
 #include "../../include/wf.h"
 #include "wf_internal.h"
+#include "wf_mx.h"
 #include "wf_rotate.h"
 
 namespace {
@@ -49,9 +50,11 @@ int log2_exact(int v) {
   return ((1 << l) == v) ? l : -1;
 }
 
-int check_pool(const wf_kv_pool* pool) {
+// mx: the call reads or writes MXFP8 keys instead of pool->k_pages, which
+// may then be NULL
+int check_pool(const wf_kv_pool* pool, const wf_mx_keys* mx = nullptr) {
   if (!pool) return fail(WF_ERR_INVALID, "pool is NULL");
-  if (!pool->k_pages || !pool->v_pages || !pool->page_table)
+  if ((!mx && !pool->k_pages) || !pool->v_pages || !pool->page_table)
     return fail(WF_ERR_INVALID, "pool: k_pages, v_pages and page_table must be non-NULL");
   if (pool->dtype != WF_BF16 && pool->dtype != WF_FP32)
     return fail(WF_ERR_INVALID, "pool: dtype %d is not WF_BF16 or WF_FP32", pool->dtype);
@@ -66,6 +69,14 @@ int check_pool(const wf_kv_pool* pool) {
                 pool->head_dim);
   if (!aligned16(pool->k_pages) || !aligned16(pool->v_pages))
     return fail(WF_ERR_INVALID, "pool: page arrays must be 16-byte aligned");
+  if (mx) {
+    if (!mx->k8_pages || !mx->k8_scales)
+      return fail(WF_ERR_INVALID, "mx keys: k8_pages and k8_scales must be non-NULL");
+    if (!aligned16(mx->k8_pages) || !aligned16(mx->k8_scales))
+      return fail(WF_ERR_INVALID, "mx keys: arrays must be 16-byte aligned");
+    if (pool->dtype != WF_BF16 || pool->head_dim != 128)
+      return fail(WF_ERR_UNSUPPORTED, "mx keys: built for bfloat16 pools with head_dim 128");
+  }
   const int64_t elems = (int64_t)pool->num_pages * pool->num_heads * pool->page_size *
                         pool->head_dim;
   if (elems > (int64_t(1) << 40))
@@ -109,7 +120,8 @@ void push_range(std::vector<int2>& r, int lo, int hi) {
 // when any group has rows.
 int launch_groups(const wf_kv_pool* pool, const std::vector<GroupSpec>& groups, const void* q,
                   int64_t q_row_stride, float scale, void* out, int64_t out_row_stride,
-                  float* lse, int64_t lse_stride, hipStream_t stream) {
+                  float* lse, int64_t lse_stride, hipStream_t stream,
+                  const wf_mx_keys* mx = nullptr) {
   int n_ranges = 0;
   bool any_rows = false;
   for (const GroupSpec& g : groups) {
@@ -166,8 +178,13 @@ int launch_groups(const wf_kv_pool* pool, const std::vector<GroupSpec>& groups, 
   hipError_t e;
   p.status = wf::status_word_ptr(&e);
   if (!p.status) return hip_fail(e, "status word");
-  e = bf16 ? wf::launch_attn_bf16(p, pool->head_dim, bm, stream)
-           : wf::launch_attn_fp32(p, pool->head_dim, bm, stream);
+  if (mx) {
+    p.k_pages = mx->k8_pages;
+    e = wf::launch_attn_mx(p, mx->k8_scales, stream);
+  } else {
+    e = bf16 ? wf::launch_attn_bf16(p, pool->head_dim, bm, stream)
+             : wf::launch_attn_fp32(p, pool->head_dim, bm, stream);
+  }
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return ok();
 }
@@ -198,11 +215,15 @@ int wf_device_status(int32_t* status, int32_t clear) {
   return ok();
 }
 
-int wf_kv_publish(const wf_kv_pool* pool, const wf_rope* rope, const void* k,
-                  int64_t k_row_stride, const void* v, int64_t v_row_stride,
-                  const int32_t* pos_thw, int32_t n_tok, int32_t dst_logical_start,
-                  void* q_inout, int64_t q_row_stride, hipStream_t stream) {
-  int rc = check_pool(pool);
+}  // extern "C"
+
+namespace {
+
+int publish_impl(const wf_kv_pool* pool, const wf_mx_keys* mx, const wf_rope* rope,
+                 const void* k, int64_t k_row_stride, const void* v, int64_t v_row_stride,
+                 const int32_t* pos_thw, int32_t n_tok, int32_t dst_logical_start,
+                 void* q_inout, int64_t q_row_stride, hipStream_t stream) {
+  int rc = check_pool(pool, mx);
   if (rc) return rc;
   if (n_tok < 0) return fail(WF_ERR_INVALID, "n_tok %d < 0", n_tok);
   if (dst_logical_start < 0)
@@ -234,7 +255,7 @@ int wf_kv_publish(const wf_kv_pool* pool, const wf_rope* rope, const void* k,
   p.k = k;
   p.v = v;
   p.q = q_inout;
-  p.k_pages = pool->k_pages;
+  p.k_pages = mx ? mx->k8_pages : pool->k_pages;
   p.v_pages = pool->v_pages;
   p.page_table = pool->page_table;
   p.pos = pos_thw;
@@ -272,16 +293,44 @@ int wf_kv_publish(const wf_kv_pool* pool, const wf_rope* rope, const void* k,
   hipError_t e;
   p.status = wf::status_word_ptr(&e);
   if (!p.status) return hip_fail(e, "status word");
-  if ((e = wf::launch_publish(p, pool->dtype, stream)) != hipSuccess)
-    return hip_fail(e, "publish launch");
+  e = mx ? wf::launch_publish_mx(p, mx->k8_scales, stream)
+         : wf::launch_publish(p, pool->dtype, stream);
+  if (e != hipSuccess) return hip_fail(e, "publish launch");
   return ok();
 }
 
-int wf_chunk_attn(const wf_kv_pool* pool, const wf_segment* segs, int32_t n_segs,
-                  const void* q, int64_t q_row_stride, const int32_t* q_slot_start,
-                  int32_t n_slots, int32_t first_slot, float scale, void* out,
-                  int64_t out_row_stride, float* lse, hipStream_t stream) {
-  int rc = check_pool(pool);
+}  // namespace
+
+extern "C" {
+
+int wf_kv_publish(const wf_kv_pool* pool, const wf_rope* rope, const void* k,
+                  int64_t k_row_stride, const void* v, int64_t v_row_stride,
+                  const int32_t* pos_thw, int32_t n_tok, int32_t dst_logical_start,
+                  void* q_inout, int64_t q_row_stride, hipStream_t stream) {
+  return publish_impl(pool, nullptr, rope, k, k_row_stride, v, v_row_stride, pos_thw, n_tok,
+                      dst_logical_start, q_inout, q_row_stride, stream);
+}
+
+// The 8-bit QK^T variant's publish ([WF] §5.5): K quantized to MXFP8.
+int wf_kv_publish_mx(const wf_kv_pool* pool, const wf_mx_keys* keys, const wf_rope* rope,
+                     const void* k, int64_t k_row_stride, const void* v, int64_t v_row_stride,
+                     const int32_t* pos_thw, int32_t n_tok, int32_t dst_logical_start,
+                     void* q_inout, int64_t q_row_stride, hipStream_t stream) {
+  if (!keys) return fail(WF_ERR_INVALID, "keys is NULL");
+  return publish_impl(pool, keys, rope, k, k_row_stride, v, v_row_stride, pos_thw, n_tok,
+                      dst_logical_start, q_inout, q_row_stride, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+int chunk_attn_impl(const wf_kv_pool* pool, const wf_mx_keys* mx, const wf_segment* segs,
+                    int32_t n_segs, const void* q, int64_t q_row_stride,
+                    const int32_t* q_slot_start, int32_t n_slots, int32_t first_slot,
+                    float scale, void* out, int64_t out_row_stride, float* lse,
+                    hipStream_t stream) {
+  int rc = check_pool(pool, mx);
   if (rc) return rc;
   if (!segs) return fail(WF_ERR_INVALID, "segs is NULL");
   if (n_segs < 1 || n_segs > 64) return fail(WF_ERR_INVALID, "n_segs %d not in [1, 64]", n_segs);
@@ -337,7 +386,30 @@ int wf_chunk_attn(const wf_kv_pool* pool, const wf_segment* segs, int32_t n_segs
     }
   }
   return launch_groups(pool, groups, q, q_row_stride, scale, out, out_row_stride, lse,
-                       total_rows, stream);
+                       total_rows, stream, mx);
+}
+
+}  // namespace
+
+extern "C" {
+
+int wf_chunk_attn(const wf_kv_pool* pool, const wf_segment* segs, int32_t n_segs,
+                  const void* q, int64_t q_row_stride, const int32_t* q_slot_start,
+                  int32_t n_slots, int32_t first_slot, float scale, void* out,
+                  int64_t out_row_stride, float* lse, hipStream_t stream) {
+  return chunk_attn_impl(pool, nullptr, segs, n_segs, q, q_row_stride, q_slot_start, n_slots,
+                         first_slot, scale, out, out_row_stride, lse, stream);
+}
+
+// The 8-bit QK^T variant ([WF] §5.5): scores from MXFP8 queries and keys.
+int wf_chunk_attn_mx(const wf_kv_pool* pool, const wf_mx_keys* keys, const wf_segment* segs,
+                     int32_t n_segs, const void* q, int64_t q_row_stride,
+                     const int32_t* q_slot_start, int32_t n_slots, int32_t first_slot,
+                     float scale, void* out, int64_t out_row_stride, float* lse,
+                     hipStream_t stream) {
+  if (!keys) return fail(WF_ERR_INVALID, "keys is NULL");
+  return chunk_attn_impl(pool, keys, segs, n_segs, q, q_row_stride, q_slot_start, n_slots,
+                         first_slot, scale, out, out_row_stride, lse, stream);
 }
 
 int wf_group_attn(const wf_kv_pool* pool, const wf_kv_run* runs, int32_t n_runs,

@@ -25,6 +25,7 @@
 
 #include "../../include/wf.h"
 #include "wf_internal.h"
+#include "wf_mx.h"
 
 namespace wf {
 namespace {
@@ -75,6 +76,34 @@ __device__ __forceinline__ void rotate_vec(uint4& v, const float2* cs) {
   }
 }
 
+// ---- MXFP8 keys (OCP microscaling: E4M3 codes, one E8M0 scale per 32
+// features) --------------------------------------------------------------
+// Shared scale code of a block whose largest magnitude is amax:
+// floor(log2 amax) - 8 + 127 clamped at 0, i.e. the float exponent field of
+// amax minus 8 (0 for zero and for amax below 2^-119).
+__device__ __forceinline__ uint32_t mx_scale_code(float amax) {
+  const int e = (int)((__float_as_uint(amax) >> 23) & 0xffu) - 8;
+  return (uint32_t)max(e, 0);
+}
+
+// E4M3 code of y (finite), nearest value with ties to even, saturating at
+// +-448; the sign of zero is kept.
+__device__ __forceinline__ uint32_t e4m3_code(float y) {
+  const uint32_t s = (__float_as_uint(y) >> 24) & 0x80u;
+  const float a = fminf(fabsf(y), 448.0f);
+  uint32_t c;
+  if (a < 0.015625f) {
+    c = (uint32_t)__builtin_rintf(a * 512.0f);   // subnormal grid, step 2^-9
+  } else {
+    // keep 3 of the 23 mantissa bits, rounding to nearest even; a carry
+    // moves into the exponent; rebias 127 -> 7
+    uint32_t b = __float_as_uint(a);
+    b += 0x7ffffu + ((b >> 20) & 1u);
+    c = (b >> 20) - (120u << 3);
+  }
+  return s | c;
+}
+
 // Streaming 16-byte loads and stores: every input byte is read once and every
 // pool byte written once, so neither is kept for reuse (nontemporal).
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -85,6 +114,40 @@ __device__ __forceinline__ uint4 ld_stream(const void* ptr) {
 
 __device__ __forceinline__ void st_stream(void* ptr, uint4 v) {
   __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), static_cast<u32x4*>(ptr));
+}
+
+// Quantize and store one rotated 8-element K vector of a bfloat16 head row
+// (D = 128: 16 vectors per row in 16 consecutive lanes; a 32-feature block
+// is 4 consecutive lanes, all active or all inactive together, like the
+// row).  `dst` is the vector's element address in the bf16 K-pool layout
+// (head 0) or null; the MXFP8 pools share that indexing, one byte per
+// element for the codes and one scale byte per 32 elements.
+__device__ __forceinline__ void mx_store(const PublishParams& p, void* k8_scales, uint4 v,
+                                         const uint16_t* dst, int h, int ps) {
+  constexpr int D = 128;
+  const uint16_t* e = reinterpret_cast<const uint16_t*>(&v);
+  float amax = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(bf16_to_f32(e[j])));
+  amax = fmaxf(amax, __shfl_xor(amax, 1));
+  amax = fmaxf(amax, __shfl_xor(amax, 2));
+  const uint32_t sc = mx_scale_code(amax);
+  const float mult = __uint_as_float((254u - sc) << 23);   // 2^(127 - sc), exact
+  uint32_t w[2] = {0u, 0u};
+#pragma unroll
+  for (int j = 0; j < 8; ++j) w[j >> 2] |= e4m3_code(bf16_to_f32(e[j]) * mult) << (8 * (j & 3));
+  // the row's four scale codes, gathered by its first lane
+  const int lane = threadIdx.x & 63, row0 = lane & ~15;
+  uint32_t word = 0u;
+#pragma unroll
+  for (int bk = 0; bk < 4; ++bk) word |= (uint32_t)__shfl((int)sc, row0 + 4 * bk) << (8 * bk);
+  if (!dst) return;
+  const int64_t idx = (dst - static_cast<const uint16_t*>(p.k_pages)) + (int64_t)h * ps * D;
+  uint8_t* codes = static_cast<uint8_t*>(p.k_pages) + idx;
+  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+  __builtin_nontemporal_store(u32x2{w[0], w[1]}, reinterpret_cast<u32x2*>(codes));
+  if ((lane & 15) == 0)
+    __builtin_nontemporal_store(word, static_cast<uint32_t*>(k8_scales) + idx / D);
 }
 
 template <int D, typename T>
@@ -114,11 +177,12 @@ __device__ __forceinline__ void tile_pages(const PublishParams& p, int L0, int l
   }
 }
 
-template <int D, bool BF16, bool HAS_Q>
+template <int D, bool BF16, bool HAS_Q, bool MX>
 __device__ __forceinline__ void k_block(
-    const PublishParams& p, int b,
+    const PublishParams& p, void* k8_scales, int b,
     PublishShared<D, typename std::conditional<BF16, uint16_t, float>::type>& sm,
     int* page_of) {
+  static_assert(!MX || (BF16 && D == 128), "MXFP8 keys: bfloat16, head_dim 128");
   using T = typename std::conditional<BF16, uint16_t, float>::type;
   constexpr int EPV = 16 / sizeof(T);        // elements per 16-byte vector
   constexpr int VPR = D / EPV;               // vectors per head row
@@ -195,7 +259,11 @@ __device__ __forceinline__ void k_block(
             *reinterpret_cast<uint4*>(qptr[i] + (int64_t)h * D) = qv[i];
           }
         }
-        if (dst[i]) st_stream(dst[i] + (int64_t)h * ps * D, kv[i]);
+        if constexpr (MX) {
+          mx_store(p, k8_scales, kv[i], dst[i], h, ps);
+        } else {
+          if (dst[i]) st_stream(dst[i] + (int64_t)h * ps * D, kv[i]);
+        }
       }
     }
   }
@@ -260,24 +328,39 @@ __device__ __forceinline__ void v_block(
   }
 }
 
-template <int D, bool BF16, bool HAS_Q>
+template <int D, bool BF16, bool HAS_Q, bool MX>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(5)))
-void publish_kernel(const PublishParams p) {
+void publish_kernel(const PublishParams p, void* k8_scales) {
   using T = typename std::conditional<BF16, uint16_t, float>::type;
   __shared__ __attribute__((aligned(16))) PublishShared<D, T> sm;
   __shared__ int page_of[kTileTok];
   const int b = blockIdx.x;
-  if (b < p.k_blocks) k_block<D, BF16, HAS_Q>(p, b, sm, page_of);
+  if (b < p.k_blocks) k_block<D, BF16, HAS_Q, MX>(p, k8_scales, b, sm, page_of);
   else v_block<D, BF16>(p, b - p.k_blocks, sm, page_of);
 }
 
 template <int D, bool BF16>
 void launch_typed(const PublishParams& p, dim3 grid, dim3 block, hipStream_t stream) {
-  if (p.q) hipLaunchKernelGGL((publish_kernel<D, BF16, true>), grid, block, 0, stream, p);
-  else hipLaunchKernelGGL((publish_kernel<D, BF16, false>), grid, block, 0, stream, p);
+  if (p.q)
+    hipLaunchKernelGGL((publish_kernel<D, BF16, true, false>), grid, block, 0, stream, p, nullptr);
+  else
+    hipLaunchKernelGGL((publish_kernel<D, BF16, false, false>), grid, block, 0, stream, p,
+                       nullptr);
 }
 
 }  // namespace
+
+hipError_t launch_publish_mx(const PublishParams& p, void* k8_scales, hipStream_t stream) {
+  const int v_blocks = p.tiles * p.heads;
+  dim3 grid(p.k_blocks + v_blocks), block(kThreads);
+  if (p.q)
+    hipLaunchKernelGGL((publish_kernel<128, true, true, true>), grid, block, 0, stream, p,
+                       k8_scales);
+  else
+    hipLaunchKernelGGL((publish_kernel<128, true, false, true>), grid, block, 0, stream, p,
+                       k8_scales);
+  return hipGetLastError();
+}
 
 hipError_t launch_publish(const PublishParams& p, int dtype, hipStream_t stream) {
   const int v_blocks = p.tiles * p.heads;

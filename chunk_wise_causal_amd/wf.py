@@ -50,6 +50,10 @@ class wf_query_group(ctypes.Structure):
                 ("run_begin", ctypes.c_int32), ("run_end", ctypes.c_int32)]
 
 
+class wf_mx_keys(ctypes.Structure):
+    _fields_ = [("k8_pages", ctypes.c_void_p), ("k8_scales", ctypes.c_void_p)]
+
+
 class wf_segment(ctypes.Structure):
     _fields_ = [("kv_start", ctypes.c_int32), ("kv_len", ctypes.c_int32),
                 ("slot", ctypes.c_int32)]
@@ -78,6 +82,15 @@ def lib() -> ctypes.CDLL:
                                     ctypes.POINTER(wf_query_group), i32, vp, i64, ctypes.c_float,
                                     vp, i64, vp, i64, vp]
         L.wf_group_attn.restype = ctypes.c_int
+        L.wf_kv_publish_mx.argtypes = [ctypes.POINTER(wf_kv_pool), ctypes.POINTER(wf_mx_keys),
+                                       ctypes.POINTER(wf_rope), vp, i64, vp, i64, vp, i32, i32,
+                                       vp, i64, vp]
+        L.wf_kv_publish_mx.restype = ctypes.c_int
+        L.wf_chunk_attn_mx.argtypes = [ctypes.POINTER(wf_kv_pool), ctypes.POINTER(wf_mx_keys),
+                                       ctypes.POINTER(wf_segment), i32, vp, i64,
+                                       ctypes.POINTER(i32), i32, i32, ctypes.c_float, vp, i64,
+                                       vp, vp]
+        L.wf_chunk_attn_mx.restype = ctypes.c_int
         L.wf_history_rotate.argtypes = [vp, i32, i32, i32, i32, i32, vp]
         L.wf_history_rotate.restype = ctypes.c_int
         L.wf_last_error.restype = ctypes.c_char_p
@@ -208,6 +221,69 @@ def wf_group_attn(pool: KVPool, runs: Sequence[Tuple[int, int]],
     rc = lib().wf_group_attn(ctypes.byref(pool.desc), rs, len(runs), gs, len(groups), _ptr(q),
                              _row_stride(q, "q"), float(scale), _ptr(out),
                              _row_stride(out, "out"), _ptr(lse), lse_stride, _stream(stream))
+    _check(rc)
+    return out
+
+
+class MXKeys:
+    """MXFP8 keys beside a pool (layout of include/wf.h): codes
+    [num_pages, H, page_size, D] uint8 and scales [num_pages, H, page_size,
+    D // 32] uint8."""
+
+    def __init__(self, codes: torch.Tensor, scales: torch.Tensor):
+        if codes.dtype != torch.uint8 or scales.dtype != torch.uint8:
+            raise ValueError("MX keys are uint8 tensors")
+        n, H, ps, D = codes.shape
+        if tuple(scales.shape) != (n, H, ps, D // 32):
+            raise ValueError("scales must be [num_pages, H, page_size, head_dim // 32]")
+        if not (codes.is_contiguous() and scales.is_contiguous()):
+            raise ValueError("MX key tensors must be contiguous")
+        self.codes, self.scales = codes, scales
+        self.desc = wf_mx_keys(codes.data_ptr(), scales.data_ptr())
+
+    @classmethod
+    def empty(cls, num_pages: int, heads: int, page_size: int, head_dim: int, device="cuda"):
+        return cls(torch.empty(num_pages, heads, page_size, head_dim, dtype=torch.uint8,
+                               device=device),
+                   torch.empty(num_pages, heads, page_size, head_dim // 32, dtype=torch.uint8,
+                               device=device))
+
+
+def wf_kv_publish_mx(pool: KVPool, keys: MXKeys, k: torch.Tensor, v: torch.Tensor,
+                     dst_start: int, pos: Optional[torch.Tensor] = None,
+                     rope: Optional[Tuple[Tuple[int, int, int], float]] = None,
+                     q: Optional[torch.Tensor] = None, stream=None) -> None:
+    """wf_kv_publish with K quantized to MXFP8 into `keys` (C: wf_kv_publish_mx)."""
+    n = k.shape[0]
+    r = None
+    if rope is not None:
+        (dt, dh, dw), theta = rope
+        r = wf_rope(dt, dh, dw, float(theta))
+    qs = _row_stride(q, "q") if q is not None else 0
+    if pos is not None and (pos.dtype != torch.int32 or not pos.is_contiguous()):
+        raise ValueError("pos must be a contiguous int32 [n, 3] tensor")
+    rc = lib().wf_kv_publish_mx(ctypes.byref(pool.desc), ctypes.byref(keys.desc),
+                                ctypes.byref(r) if r else None, _ptr(k), _row_stride(k, "k"),
+                                _ptr(v), _row_stride(v, "v"), _ptr(pos), n, dst_start, _ptr(q),
+                                qs, _stream(stream))
+    _check(rc)
+
+
+def wf_chunk_attn_mx(pool: KVPool, keys: MXKeys, segments: Sequence[Tuple[int, int, int]],
+                     q: torch.Tensor, q_slot_start: Sequence[int], first_slot: int = 0,
+                     scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                     lse: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Chunk-wise causal attention with the 8-bit QK^T (C: wf_chunk_attn_mx)."""
+    if out is None:
+        out = torch.empty_like(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    segs = (wf_segment * len(segments))(*[wf_segment(*s) for s in segments])
+    qss = (ctypes.c_int32 * len(q_slot_start))(*q_slot_start)
+    rc = lib().wf_chunk_attn_mx(ctypes.byref(pool.desc), ctypes.byref(keys.desc), segs,
+                                len(segments), _ptr(q), _row_stride(q, "q"), qss,
+                                len(q_slot_start) - 1, first_slot, float(scale), _ptr(out),
+                                _row_stride(out, "out"), _ptr(lse), _stream(stream))
     _check(rc)
     return out
 

@@ -273,6 +273,54 @@ int wf_group_attn(const wf_kv_pool* pool,
                   void* out, int64_t out_row_stride,
                   float* lse, int64_t lse_stride, hipStream_t stream);
 
+/* ----- 8-bit keys and scores ([WF] §5.5: the pages also run attention with
+ * 8-bit QK^T, Sage + W8A8) ------------------------------------------------
+ *
+ * MXFP8 (OCP microscaling FP8): every token's head vector of K is stored as
+ * FP8 E4M3 codes with one power-of-two scale per 32 consecutive features:
+ *   k8_pages   device uint8 [num_pages][num_heads][page_size][head_dim]
+ *              E4M3 codes (sign, 4 exponent bits with bias 7, 3 mantissa
+ *              bits; no infinities; 0x7F/0xFF are NaN; largest finite 448)
+ *   k8_scales  device uint8 [num_pages][num_heads][page_size][head_dim / 32]
+ *              biased exponents e (E8M0): the block's scale is 2^(e - 127)
+ * They share the pool's page table and page geometry; both 16-byte aligned.
+ * Quantization of a block v[0..31]: e = floor(log2 max|v|) - 8 + 127,
+ * clamped to [0, 254] (0 for an all-zero block); code_i = the E4M3 value
+ * nearest to v_i / 2^(e - 127), ties to even, saturating at +-448.
+ * Built for bfloat16 pools with head_dim 128 (else WF_ERR_UNSUPPORTED).
+ */
+typedef struct {
+  void* k8_pages;
+  void* k8_scales;
+} wf_mx_keys;
+
+/* wf_kv_publish_mx — wf_kv_publish for the 8-bit variant: K is rotated and
+ * rounded to bfloat16 exactly as wf_kv_publish stores it, then quantized to
+ * MXFP8 into `keys` (codes and scales of every published row and head); V
+ * goes to pool->v_pages as in wf_kv_publish, and q_inout is rotated the same
+ * way.  pool->k_pages is neither read nor written and may be NULL.  Other
+ * arguments, aliasing and errors as wf_kv_publish; `keys` must not overlap
+ * the inputs. */
+int wf_kv_publish_mx(const wf_kv_pool* pool, const wf_mx_keys* keys, const wf_rope* rope,
+                     const void* k, int64_t k_row_stride,
+                     const void* v, int64_t v_row_stride,
+                     const int32_t* pos_thw, int32_t n_tok, int32_t dst_logical_start,
+                     void* q_inout, int64_t q_row_stride, hipStream_t stream);
+
+/* wf_chunk_attn_mx — wf_chunk_attn with the 8-bit QK^T: for every visible
+ * key L, z_L = scale * <mx(q[i][h]), mx(K_L[h])>, where mx(K) are the
+ * pool's MXFP8 keys (written by wf_kv_publish_mx) and mx(q) is the bfloat16
+ * query quantized by the same rule, per row, head and 32-feature block,
+ * inside the call.  Softmax, P V (bfloat16 probabilities, float32
+ * accumulation), out and lse as in wf_chunk_attn.  pool->k_pages is not read
+ * and may be NULL.  Other arguments, aliasing and errors as wf_chunk_attn. */
+int wf_chunk_attn_mx(const wf_kv_pool* pool, const wf_mx_keys* keys,
+                     const wf_segment* segs, int32_t n_segs,
+                     const void* q, int64_t q_row_stride,
+                     const int32_t* q_slot_start, int32_t n_slots, int32_t first_slot,
+                     float scale, void* out, int64_t out_row_stride, float* lse,
+                     hipStream_t stream);
+
 /* ------------------------------------------------------------------------
  * wf_history_rotate — end-of-round history rotation by page-table edits
  * ([WF] §3.1: the context holds a bounded clean history, oldest first,

@@ -241,3 +241,49 @@ def test_history_rotate_single_chunk_is_noop(L):
     assert rotate(L, n=1) == (wf.WF_OK, "")
     # the window may end exactly at the table's end
     assert rotate(L, nlp=14, n=1)[0] == wf.WF_OK
+
+
+def mxkeys(**kw):
+    d = dict(k8_pages=FAKE + 0x400000, k8_scales=FAKE + 0x500000)
+    d.update(kw)
+    return wf.wf_mx_keys(**d)
+
+
+@pytest.mark.parametrize("keys,pkw,code,msg", [
+    (None, {}, wf.WF_ERR_INVALID, "keys is NULL"),
+    (dict(k8_pages=None), {}, wf.WF_ERR_INVALID, "k8_pages and k8_scales"),
+    (dict(k8_scales=None), {}, wf.WF_ERR_INVALID, "k8_pages and k8_scales"),
+    (dict(k8_scales=FAKE + 0x500004), {}, wf.WF_ERR_INVALID, "aligned"),
+    ({}, dict(dtype=wf.WF_FP32), wf.WF_ERR_UNSUPPORTED, "mx keys"),
+    ({}, dict(head_dim=64), wf.WF_ERR_UNSUPPORTED, "mx keys"),
+    ({}, dict(v_pages=None), wf.WF_ERR_INVALID, "non-NULL"),
+])
+def test_mx_calls_reject(L, keys, pkw, code, msg):
+    p = pool(**pkw)
+    kp = None if keys is None else ctypes.byref(mxkeys(**keys))
+    rope = wf.wf_rope(44, 42, 42, 1e4) if p.head_dim == 128 else wf.wf_rope(24, 20, 20, 1e4)
+    rc = L.wf_kv_publish_mx(ctypes.byref(p), kp, ctypes.byref(rope), FAKE, 512, FAKE, 512, FAKE,
+                            100, 0, None, 0, None)
+    err = L.wf_last_error().decode()
+    assert rc == code and msg in err, (rc, err)
+    segs = (wf.wf_segment * 2)(wf.wf_segment(0, 100, -1), wf.wf_segment(100, 50, 0))
+    qss = (ctypes.c_int32 * 2)(0, 50)
+    rc = L.wf_chunk_attn_mx(ctypes.byref(p), kp, segs, 2, FAKE, 512, qss, 1, 0,
+                            ctypes.c_float(0.088), FAKE, 512, None, None)
+    err = L.wf_last_error().decode()
+    assert rc == code and msg in err, (rc, err)
+
+
+def test_mx_calls_need_no_bf16_keys(L):
+    # the 8-bit calls never touch pool.k_pages: NULL is accepted (no-op calls)
+    p = pool(k_pages=None)
+    k = mxkeys()
+    assert L.wf_kv_publish_mx(ctypes.byref(p), ctypes.byref(k), None, FAKE, 512, FAKE, 512,
+                              None, 0, 0, None, 0, None) == wf.WF_OK
+    segs = (wf.wf_segment * 1)(wf.wf_segment(0, 100, 0))
+    qss = (ctypes.c_int32 * 2)(0, 0)
+    assert L.wf_chunk_attn_mx(ctypes.byref(p), ctypes.byref(k), segs, 1, FAKE, 512, qss, 1, 0,
+                              ctypes.c_float(0.088), FAKE, 512, None, None) == wf.WF_OK
+    # the bfloat16 calls still require it
+    assert L.wf_kv_publish(ctypes.byref(p), None, FAKE, 512, FAKE, 512, None, 0, 0, None, 0,
+                           None) == wf.WF_ERR_INVALID
