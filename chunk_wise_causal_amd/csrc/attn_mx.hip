@@ -480,11 +480,13 @@ __device__ __forceinline__ void interleave_qk_softmax() {
   constexpr int NDS = Frag<D>::SB * (2 * Frag<D>::DK + 1);   // code chunks + scale words
   constexpr int AHEAD = 3;
   constexpr int VPM = 24;                                // VALU per MFMA
+  // (the block-scaled product is not in the hints' matrix class, so the
+  // groups name only the vector work and the reads between the products;
+  // the scheduler places the products among them)
 #pragma unroll
   for (int k = 0; k < AHEAD; ++k) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
 #pragma unroll
   for (int k = 0; k < NM; ++k) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);
     if (AHEAD + 2 * k < NDS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     if (AHEAD + 2 * k + 1 < NDS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
