@@ -156,6 +156,50 @@ def cpu_baseline(cfg, seconds: float):
     }
 
 
+def time_mx_variant(cfg, torch, wf, q, k, v, pos, pool, out, steps: int):
+    """The 8-bit QK^T variant on the same inputs: wf_kv_publish_mx of the
+    round, then wf_chunk_attn_mx, timed per step with HIP events on the
+    launch stream.  TFLOP/s count the same unmasked FLOPs; half of them (QK^T)
+    run at the FP8 rate, so the matching peak is 2 / (1/5000 + 1/2500)
+    TFLOP/s."""
+    keys = wf.MXKeys.empty(cfg.n_pages, cfg.heads, cfg.page_size, cfg.head_dim)
+    rope = (cfg.rope, cfg.theta)
+    ss = cfg.store_start
+    stream = torch.cuda.current_stream()
+    wf.wf_kv_publish_mx(pool, keys, k[:ss], v[:ss], 0, pos=pos[:ss], rope=rope, stream=stream)
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        wf.wf_kv_publish_mx(pool, keys, k[ss:], v[ss:], ss, pos=pos[ss:], rope=rope,
+                            stream=stream)
+        if ev:
+            ev[1].record(stream)
+        wf.wf_chunk_attn_mx(pool, keys, cfg.segments(), q, cfg.q_slot_start(), 0, cfg.scale,
+                            out=out, stream=stream)
+        if ev:
+            ev[2].record(stream)
+
+    for _ in range(2):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    assert wf.wf_device_status() == 0
+    pub = float(np.median([e[0].elapsed_time(e[1]) for e in evs]))
+    att = float(np.median([e[1].elapsed_time(e[2]) for e in evs]))
+    tf = cfg.unmasked_flops() / (att * 1e-3) / 1e12
+    mixed_peak = 2.0 / (1.0 / 5000.0 + 1.0 / PEAK_BF16_TFLOPS)
+    return {"attn_ms_p50": round(att, 4), "attn_tflops": round(tf, 2),
+            "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+            "frac_fp8_bf16_peak": round(tf / mixed_peak, 4), "fp8_bf16_peak": round(mixed_peak, 1),
+            "publish_ms_p50": round(pub, 4),
+            "kernel": "attn_fwd_mx<128, true>",
+            "format": "MXFP8 (E4M3, E8M0 per 32 features) Q and K; bf16 P V"}
+
+
 def time_history_rotate(cfg, torch, wf, reps: int = 200):
     """End-of-round history rotation (wf_history_rotate) on the page-aligned
     placement of the same context: average launch duration over `reps`
@@ -275,6 +319,7 @@ def main():
         "cpu_baseline": None,
     }
     res["history_rotate"] = time_history_rotate(cfg, torch, wf)
+    res["mx_variant"] = time_mx_variant(cfg, torch, wf, q, k, v, pos, pool, out, args.steps)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
     print(json.dumps(res), flush=True)
