@@ -23,6 +23,8 @@ Modules:
   history    end-of-round history rotation as a page-table reordering
   mx         MXFP8 (E4M3 + E8M0 block scale) keys and queries for the
              8-bit QK^T variant, and its attention
+  qkv        QKV projection (one float64 product, one rounding) followed
+             by the publish: what the fused projection epilogue must produce
 
 Parity status: every function here is pinned by tests/test_oracle_*.py
 against closed forms, textbook/library special cases, invariants the pages
