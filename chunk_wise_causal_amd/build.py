@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libwf.so")
 SOURCES = ["api.cpp", "status.hip", "publish.hip", "attn_bf16.hip", "attn_fp32.hip",
-           "rotate.hip", "attn_mx.hip"]
+           "rotate.hip", "attn_mx.hip", "qkv_gemm.hip"]
 ARCH = "gfx950"
 
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

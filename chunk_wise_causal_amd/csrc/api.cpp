@@ -17,6 +17,7 @@
 #include "../../include/wf.h"
 #include "wf_internal.h"
 #include "wf_mx.h"
+#include "wf_qkv.h"
 #include "wf_rotate.h"
 
 namespace {
@@ -82,6 +83,32 @@ int check_pool(const wf_kv_pool* pool, const wf_mx_keys* mx = nullptr) {
   if (elems > (int64_t(1) << 40))
     return fail(WF_ERR_UNSUPPORTED, "pool: too large");
   return WF_OK;
+}
+
+int check_rope(const wf_kv_pool* pool, const wf_rope* rope, int32_t n_tok,
+               const int32_t* pos_thw) {
+  if (!rope) return WF_OK;
+  if (rope->d_t < 0 || rope->d_h < 0 || rope->d_w < 0 || (rope->d_t & 1) || (rope->d_h & 1) ||
+      (rope->d_w & 1))
+    return fail(WF_ERR_INVALID, "rope: sub-band widths must be even and >= 0");
+  if (rope->d_t + rope->d_h + rope->d_w != pool->head_dim)
+    return fail(WF_ERR_INVALID, "rope: d_t + d_h + d_w = %d != head_dim %d",
+                rope->d_t + rope->d_h + rope->d_w, pool->head_dim);
+  if (!(rope->theta > 0.0) || !std::isfinite(rope->theta))
+    return fail(WF_ERR_INVALID, "rope: theta must be finite and > 0");
+  if (n_tok > 0 && !pos_thw) return fail(WF_ERR_INVALID, "pos_thw is NULL with rope");
+  return WF_OK;
+}
+
+// frequencies of every pair: theta^(-2i/d_a), evaluated in double
+void fill_pairs(const wf_rope* rope, int32_t* axis, double* omega) {
+  const int d[3] = {rope->d_t, rope->d_h, rope->d_w};
+  int pair = 0;
+  for (int a = 0; a < 3; ++a)
+    for (int i = 0; i < d[a] / 2; ++i, ++pair) {
+      axis[pair] = a;
+      omega[pair] = std::pow(rope->theta, (-2.0 * i) / (double)d[a]);
+    }
 }
 
 int check_rows(const char* name, const void* ptr, int64_t stride, const wf_kv_pool* pool) {
@@ -233,17 +260,7 @@ int publish_impl(const wf_kv_pool* pool, const wf_mx_keys* mx, const wf_rope* ro
     return fail(WF_ERR_INVALID, "dst_logical_start + n_tok = %lld exceeds pool capacity %lld",
                 (long long)dst_logical_start + n_tok, (long long)cap);
   wf::PublishParams p{};
-  if (rope) {
-    if (rope->d_t < 0 || rope->d_h < 0 || rope->d_w < 0 || (rope->d_t & 1) ||
-        (rope->d_h & 1) || (rope->d_w & 1))
-      return fail(WF_ERR_INVALID, "rope: sub-band widths must be even and >= 0");
-    if (rope->d_t + rope->d_h + rope->d_w != pool->head_dim)
-      return fail(WF_ERR_INVALID, "rope: d_t + d_h + d_w = %d != head_dim %d",
-                  rope->d_t + rope->d_h + rope->d_w, pool->head_dim);
-    if (!(rope->theta > 0.0) || !std::isfinite(rope->theta))
-      return fail(WF_ERR_INVALID, "rope: theta must be finite and > 0");
-    if (n_tok > 0 && !pos_thw) return fail(WF_ERR_INVALID, "pos_thw is NULL with rope");
-  }
+  if ((rc = check_rope(pool, rope, n_tok, pos_thw))) return rc;
   if (q_inout && !rope) return fail(WF_ERR_INVALID, "q_inout requires rope");
   if (n_tok > 0) {
     if ((rc = check_rows("k", k, k_row_stride, pool))) return rc;
@@ -270,16 +287,7 @@ int publish_impl(const wf_kv_pool* pool, const wf_mx_keys* mx, const wf_rope* ro
   p.num_pages = pool->num_pages;
   p.num_logical_pages = pool->num_logical_pages;
   p.rope = rope ? 1 : 0;
-  if (rope) {
-    // frequencies of every pair: theta^(-2i/d_a), evaluated in double
-    const int d[3] = {rope->d_t, rope->d_h, rope->d_w};
-    int pair = 0;
-    for (int a = 0; a < 3; ++a)
-      for (int i = 0; i < d[a] / 2; ++i, ++pair) {
-        p.pair_axis[pair] = a;
-        p.pair_omega[pair] = std::pow(rope->theta, (-2.0 * i) / (double)d[a]);
-      }
-  }
+  if (rope) fill_pairs(rope, p.pair_axis, p.pair_omega);
   // 64-token tiles of the window; K blocks take up to 8 heads (the rotary
   // factors of a tile are evaluated once per K block), V blocks one head
   const int64_t tiles = ((int64_t)dst_logical_start + n_tok - 1) / 64 - dst_logical_start / 64 + 1;
@@ -511,6 +519,70 @@ int wf_history_rotate(int32_t* page_table, int32_t num_logical_pages, int32_t pa
   if (n_chunks == 1) return ok();
   const hipError_t e = wf::launch_rotate(page_table, (int)first, (int)n, (int)cp, stream);
   if (e != hipSuccess) return hip_fail(e, "rotation launch");
+  return ok();
+}
+
+// The QKV projection with the publish fused into its epilogue ([WF] §4.2:
+// K/V are published right after the projection and RoPE).
+int wf_qkv_publish(const wf_kv_pool* pool, const wf_rope* rope, const void* x,
+                   int64_t x_row_stride, int32_t hidden, const void* w_qkv, const void* bias,
+                   const int32_t* pos_thw, int32_t n_tok, int32_t dst_logical_start,
+                   void* q_out, int64_t q_row_stride, hipStream_t stream) {
+  int rc = check_pool(pool);
+  if (rc) return rc;
+  if (pool->dtype != WF_BF16 || pool->head_dim != 128)
+    return fail(WF_ERR_UNSUPPORTED, "qkv publish: built for bfloat16 pools with head_dim 128");
+  if (n_tok < 0) return fail(WF_ERR_INVALID, "n_tok %d < 0", n_tok);
+  if (dst_logical_start < 0)
+    return fail(WF_ERR_INVALID, "dst_logical_start %d < 0", dst_logical_start);
+  const int64_t cap = (int64_t)pool->num_logical_pages * pool->page_size;
+  if ((int64_t)dst_logical_start + n_tok > cap)
+    return fail(WF_ERR_INVALID, "dst_logical_start + n_tok = %lld exceeds pool capacity %lld",
+                (long long)dst_logical_start + n_tok, (long long)cap);
+  if (hidden < 64 || hidden % 64 != 0)
+    return fail(WF_ERR_UNSUPPORTED, "hidden %d is not a positive multiple of 64", hidden);
+  if ((rc = check_rope(pool, rope, n_tok, pos_thw))) return rc;
+  if (n_tok > 0) {
+    if (!x || !w_qkv) return fail(WF_ERR_INVALID, "x and w_qkv must be non-NULL");
+    if (!aligned16(x) || !aligned16(w_qkv))
+      return fail(WF_ERR_INVALID, "x and w_qkv must be 16-byte aligned");
+    if (x_row_stride < hidden || x_row_stride % 8 != 0)
+      return fail(WF_ERR_INVALID, "x_row_stride %lld must be >= hidden and a multiple of 8",
+                  (long long)x_row_stride);
+    if (bias && (reinterpret_cast<uintptr_t>(bias) & 1u))
+      return fail(WF_ERR_INVALID, "bias must be 2-byte aligned");
+    if (q_out && (rc = check_rows("q", q_out, q_row_stride, pool))) return rc;
+  }
+  if (n_tok == 0) return ok();
+  wf::QkvParams p{};
+  p.x = static_cast<const uint16_t*>(x);
+  p.w = static_cast<const uint16_t*>(w_qkv);
+  p.bias = static_cast<const uint16_t*>(bias);
+  p.q_out = static_cast<uint16_t*>(q_out);
+  p.k_pages = static_cast<uint16_t*>(pool->k_pages);
+  p.v_pages = static_cast<uint16_t*>(pool->v_pages);
+  p.page_table = pool->page_table;
+  p.pos = pos_thw;
+  p.x_stride = x_row_stride;
+  p.q_stride = q_out ? q_row_stride : 0;
+  p.n_tok = n_tok;
+  p.hidden = hidden;
+  p.dst_start = dst_logical_start;
+  p.heads = pool->num_heads;
+  p.ps_log2 = log2_exact(pool->page_size);
+  p.num_pages = pool->num_pages;
+  p.tok_tiles = (n_tok + 127) / 128;
+  p.sec0 = q_out ? 0 : 1;
+  p.feat_tiles = (3 - p.sec0) * pool->num_heads;
+  p.rope = rope ? 1 : 0;
+  if (rope) fill_pairs(rope, p.pair_axis, p.pair_omega);
+  if ((int64_t)p.feat_tiles * p.tok_tiles > 0x7fffffff)
+    return fail(WF_ERR_UNSUPPORTED, "projection too large");
+  hipError_t e;
+  p.status = wf::status_word_ptr(&e);
+  if (!p.status) return hip_fail(e, "status word");
+  if ((e = wf::launch_qkv_publish(p, stream)) != hipSuccess)
+    return hip_fail(e, "qkv publish launch");
   return ok();
 }
 

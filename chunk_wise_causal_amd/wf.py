@@ -91,6 +91,9 @@ def lib() -> ctypes.CDLL:
                                        ctypes.POINTER(i32), i32, i32, ctypes.c_float, vp, i64,
                                        vp, vp]
         L.wf_chunk_attn_mx.restype = ctypes.c_int
+        L.wf_qkv_publish.argtypes = [ctypes.POINTER(wf_kv_pool), ctypes.POINTER(wf_rope), vp, i64,
+                                     i32, vp, vp, vp, i32, i32, vp, i64, vp]
+        L.wf_qkv_publish.restype = ctypes.c_int
         L.wf_history_rotate.argtypes = [vp, i32, i32, i32, i32, i32, vp]
         L.wf_history_rotate.restype = ctypes.c_int
         L.wf_last_error.restype = ctypes.c_char_p
@@ -286,6 +289,31 @@ def wf_chunk_attn_mx(pool: KVPool, keys: MXKeys, segments: Sequence[Tuple[int, i
                                 _row_stride(out, "out"), _ptr(lse), _stream(stream))
     _check(rc)
     return out
+
+
+def wf_qkv_publish(pool: KVPool, x: torch.Tensor, w_qkv: torch.Tensor, dst_start: int,
+                   pos: Optional[torch.Tensor] = None,
+                   rope: Optional[Tuple[Tuple[int, int, int], float]] = None,
+                   bias: Optional[torch.Tensor] = None, q_out: Optional[torch.Tensor] = None,
+                   stream=None) -> None:
+    """QKV projection of x [n, hidden] with w_qkv [3*H*D, hidden] (+ bias),
+    published like wf_kv_publish; the rotated Q goes to q_out [n, H, D]
+    if given (C: wf_qkv_publish)."""
+    if x.dim() != 2 or x.stride(1) != 1 or w_qkv.dim() != 2 or not w_qkv.is_contiguous():
+        raise ValueError("x: [n, hidden] with contiguous rows; w_qkv: contiguous [3*H*D, hidden]")
+    if bias is not None and not bias.is_contiguous():
+        raise ValueError("bias must be contiguous")
+    if pos is not None and (pos.dtype != torch.int32 or not pos.is_contiguous()):
+        raise ValueError("pos must be a contiguous int32 [n, 3] tensor")
+    r = None
+    if rope is not None:
+        (dt, dh, dw), theta = rope
+        r = wf_rope(dt, dh, dw, float(theta))
+    qs = _row_stride(q_out, "q_out") if q_out is not None else 0
+    rc = lib().wf_qkv_publish(ctypes.byref(pool.desc), ctypes.byref(r) if r else None, _ptr(x),
+                              x.stride(0), x.shape[1], _ptr(w_qkv), _ptr(bias), _ptr(pos),
+                              x.shape[0], dst_start, _ptr(q_out), qs, _stream(stream))
+    _check(rc)
 
 
 def wf_history_rotate(pool: KVPool, window_start: int, chunk_stride: int, n_chunks: int,

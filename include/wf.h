@@ -273,6 +273,44 @@ int wf_group_attn(const wf_kv_pool* pool,
                   void* out, int64_t out_row_stride,
                   float* lse, int64_t lse_stride, hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * wf_qkv_publish — the QKV projection with the publish fused into its
+ * epilogue ([WF] §4.2: K/V are published right after the QKV projection and
+ * RoPE).  Projected K and V go straight from the accumulators into the pool;
+ * they are never stored as a dense tensor and read back.
+ *
+ * For t in [0, n_tok), output feature f in [0, 3*H*D):
+ *   qkv[t][f] = bf16( sum_k x[t][k] * w_qkv[f][k]  (+ bias[f]) )
+ * computed with float32 accumulation and rounded once to bfloat16 (the
+ * output of an unfused bfloat16 projection); features [0, H*D) are Q,
+ * [H*D, 2*H*D) K and [2*H*D, 3*H*D) V, each [H][D].  Then, exactly as
+ * wf_kv_publish with these K and V at dst_logical_start (and q_inout = Q):
+ * K and Q are rotated by the 3D RoPE (if rope), K and V are scattered into
+ * the pool, and the rotated Q is written to q_out.
+ *
+ *   pool            bfloat16 pool with head_dim 128 (else WF_ERR_UNSUPPORTED)
+ *   rope, pos_thw   as in wf_kv_publish
+ *   x               device bf16 [n_tok] rows of [hidden]; 16-byte aligned,
+ *                   x_row_stride >= hidden and a multiple of 8 (elements)
+ *   hidden          a positive multiple of 64 (else WF_ERR_UNSUPPORTED)
+ *   w_qkv           device bf16 [3*H*D][hidden], rows contiguous (the layout
+ *                   of a fused linear layer's weight); 16-byte aligned
+ *   bias            device bf16 [3*H*D], nullable
+ *   n_tok, dst_logical_start   as in wf_kv_publish
+ *   q_out           device bf16 [n_tok] rows of [H][D], nullable (Q is then
+ *                   not computed); q_row_stride as for q in wf_kv_publish
+ * The float32 accumulation order is the kernel's own, so a value within
+ * float32 rounding of a bfloat16 rounding boundary may round to the other
+ * neighbour than a different summation order would.
+ * Aliasing: no output may overlap x, w_qkv, bias or each other.
+ * Returns WF_OK, WF_ERR_INVALID, WF_ERR_UNSUPPORTED or WF_ERR_HIP.
+ */
+int wf_qkv_publish(const wf_kv_pool* pool, const wf_rope* rope,
+                   const void* x, int64_t x_row_stride, int32_t hidden,
+                   const void* w_qkv, const void* bias,
+                   const int32_t* pos_thw, int32_t n_tok, int32_t dst_logical_start,
+                   void* q_out, int64_t q_row_stride, hipStream_t stream);
+
 /* ----- 8-bit keys and scores ([WF] §5.5: the pages also run attention with
  * 8-bit QK^T, Sage + W8A8) ------------------------------------------------
  *

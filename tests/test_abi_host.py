@@ -287,3 +287,37 @@ def test_mx_calls_need_no_bf16_keys(L):
     # the bfloat16 calls still require it
     assert L.wf_kv_publish(ctypes.byref(p), None, FAKE, 512, FAKE, 512, None, 0, 0, None, 0,
                            None) == wf.WF_ERR_INVALID
+
+
+def qkv(L, p=None, rope=wf.wf_rope(44, 42, 42, 1e4), x=FAKE, xs=5120, hidden=5120, w=FAKE,
+        bias=None, pos=FAKE, n=100, dst=0, q=FAKE, qs=512):
+    p = p or pool()
+    rc = L.wf_qkv_publish(ctypes.byref(p), ctypes.byref(rope) if rope else None, x, xs, hidden,
+                          w, bias, pos, n, dst, q, qs, None)
+    return rc, L.wf_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(p=pool(dtype=wf.WF_FP32)), wf.WF_ERR_UNSUPPORTED, "bfloat16"),
+    (dict(p=pool(head_dim=64)), wf.WF_ERR_UNSUPPORTED, "head_dim 128"),
+    (dict(hidden=100, xs=104), wf.WF_ERR_UNSUPPORTED, "multiple of 64"),
+    (dict(hidden=0, xs=0), wf.WF_ERR_UNSUPPORTED, "multiple of 64"),
+    (dict(x=None), wf.WF_ERR_INVALID, "non-NULL"),
+    (dict(w=None), wf.WF_ERR_INVALID, "non-NULL"),
+    (dict(w=FAKE + 8), wf.WF_ERR_INVALID, "aligned"),
+    (dict(xs=5000), wf.WF_ERR_INVALID, "x_row_stride"),
+    (dict(xs=5124), wf.WF_ERR_INVALID, "x_row_stride"),
+    (dict(bias=FAKE + 1), wf.WF_ERR_INVALID, "bias"),
+    (dict(pos=None), wf.WF_ERR_INVALID, "pos_thw"),
+    (dict(rope=wf.wf_rope(44, 42, 40, 1e4)), wf.WF_ERR_INVALID, "head_dim"),
+    (dict(n=-1), wf.WF_ERR_INVALID, "n_tok"),
+    (dict(dst=2500), wf.WF_ERR_INVALID, "capacity"),
+    (dict(qs=100), wf.WF_ERR_INVALID, "q_row_stride"),
+])
+def test_qkv_publish_rejects(L, kw, code, msg):
+    rc, err = qkv(L, **kw)
+    assert rc == code and msg in err, (rc, err)
+
+
+def test_qkv_publish_zero_tokens_is_noop(L):
+    assert qkv(L, n=0, x=None, w=None)[0] == wf.WF_OK
