@@ -539,8 +539,8 @@ int wf_qkv_publish(const wf_kv_pool* pool, const wf_rope* rope, const void* x,
   if ((int64_t)dst_logical_start + n_tok > cap)
     return fail(WF_ERR_INVALID, "dst_logical_start + n_tok = %lld exceeds pool capacity %lld",
                 (long long)dst_logical_start + n_tok, (long long)cap);
-  if (hidden < 64 || hidden % 64 != 0)
-    return fail(WF_ERR_UNSUPPORTED, "hidden %d is not a positive multiple of 64", hidden);
+  if (hidden < 64 || hidden % 64 != 0 || hidden > 65536)
+    return fail(WF_ERR_UNSUPPORTED, "hidden %d is not a multiple of 64 in [64, 65536]", hidden);
   if ((rc = check_rope(pool, rope, n_tok, pos_thw))) return rc;
   if (n_tok > 0) {
     if (!x || !w_qkv) return fail(WF_ERR_INVALID, "x and w_qkv must be non-NULL");
@@ -549,6 +549,8 @@ int wf_qkv_publish(const wf_kv_pool* pool, const wf_rope* rope, const void* x,
     if (x_row_stride < hidden || x_row_stride % 8 != 0)
       return fail(WF_ERR_INVALID, "x_row_stride %lld must be >= hidden and a multiple of 8",
                   (long long)x_row_stride);
+    if (x_row_stride > (int64_t(1) << 22))
+      return fail(WF_ERR_UNSUPPORTED, "x_row_stride %lld exceeds 2^22", (long long)x_row_stride);
     if (bias && (reinterpret_cast<uintptr_t>(bias) & 1u))
       return fail(WF_ERR_INVALID, "bias must be 2-byte aligned");
     if (q_out && (rc = check_rows("q", q_out, q_row_stride, pool))) return rc;
@@ -571,7 +573,7 @@ int wf_qkv_publish(const wf_kv_pool* pool, const wf_rope* rope, const void* x,
   p.heads = pool->num_heads;
   p.ps_log2 = log2_exact(pool->page_size);
   p.num_pages = pool->num_pages;
-  p.tok_tiles = (n_tok + 127) / 128;
+  p.tok_tiles = (n_tok + 255) / 256;
   p.sec0 = q_out ? 0 : 1;
   p.feat_tiles = (3 - p.sec0) * pool->num_heads;
   p.rope = rope ? 1 : 0;

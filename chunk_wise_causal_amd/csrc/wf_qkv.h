@@ -18,7 +18,7 @@ struct QkvParams {
   int* status;
   int64_t x_stride, q_stride; // elements between rows
   int32_t n_tok, hidden, dst_start, heads, ps_log2, num_pages;
-  int32_t tok_tiles;          // ceil(n_tok / 128)
+  int32_t tok_tiles;          // ceil(n_tok / 256)
   int32_t feat_tiles;         // 128-feature tiles computed (2H without Q, 3H with)
   int32_t sec0;               // section of the first tile: 0 (Q) or 1 (K)
   int32_t rope;               // 0/1

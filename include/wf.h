@@ -292,7 +292,8 @@ int wf_group_attn(const wf_kv_pool* pool,
  *   rope, pos_thw   as in wf_kv_publish
  *   x               device bf16 [n_tok] rows of [hidden]; 16-byte aligned,
  *                   x_row_stride >= hidden and a multiple of 8 (elements)
- *   hidden          a positive multiple of 64 (else WF_ERR_UNSUPPORTED)
+ *   hidden          a multiple of 64 in [64, 65536], x_row_stride at most
+ *                   2^22 (else WF_ERR_UNSUPPORTED)
  *   w_qkv           device bf16 [3*H*D][hidden], rows contiguous (the layout
  *                   of a fused linear layer's weight); 16-byte aligned
  *   bias            device bf16 [3*H*D], nullable

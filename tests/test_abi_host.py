@@ -302,6 +302,8 @@ def qkv(L, p=None, rope=wf.wf_rope(44, 42, 42, 1e4), x=FAKE, xs=5120, hidden=512
     (dict(p=pool(head_dim=64)), wf.WF_ERR_UNSUPPORTED, "head_dim 128"),
     (dict(hidden=100, xs=104), wf.WF_ERR_UNSUPPORTED, "multiple of 64"),
     (dict(hidden=0, xs=0), wf.WF_ERR_UNSUPPORTED, "multiple of 64"),
+    (dict(hidden=65600, xs=65600), wf.WF_ERR_UNSUPPORTED, "multiple of 64"),
+    (dict(xs=(1 << 22) + 8), wf.WF_ERR_UNSUPPORTED, "2^22"),
     (dict(x=None), wf.WF_ERR_INVALID, "non-NULL"),
     (dict(w=None), wf.WF_ERR_INVALID, "non-NULL"),
     (dict(w=FAKE + 8), wf.WF_ERR_INVALID, "aligned"),
