@@ -200,6 +200,56 @@ def time_mx_variant(cfg, torch, wf, q, k, v, pos, pool, out, steps: int):
             "format": "MXFP8 (E4M3, E8M0 per 32 features) Q and K; bf16 P V"}
 
 
+def time_qkv_publish(cfg, torch, wf, pos, steps: int):
+    """The QKV projection of the round's tokens (hidden = heads x head_dim)
+    with the publish fused into its epilogue (wf_qkv_publish), against the
+    unfused order: the same projection by torch's GEMM, then wf_kv_publish.
+    Synthetic bf16 hidden states and weights drawn on the device."""
+    H, D = cfg.heads, cfg.head_dim
+    hid, n, ss = H * D, cfg.tick_tokens, cfg.store_start
+    g = torch.Generator(device="cuda").manual_seed(cfg.seed + 7)
+    x = torch.randn(n, hid, device="cuda", generator=g).to(torch.bfloat16)
+    w = (torch.randn(3 * hid, hid, device="cuda", generator=g) / hid ** 0.5).to(torch.bfloat16)
+    b = (torch.randn(3 * hid, device="cuda", generator=g) * 0.1).to(torch.bfloat16)
+    table = torch.randperm(cfg.n_logical_pages, device="cuda", generator=g).to(torch.int32)
+    qpool = wf.KVPool.empty(cfg.n_logical_pages, H, cfg.page_size, D, table)
+    q_out = torch.empty(n, H, D, dtype=torch.bfloat16, device="cuda")
+    rope = (cfg.rope, cfg.theta)
+    p = pos[ss:]
+    stream = torch.cuda.current_stream()
+
+    def fused():
+        wf.wf_qkv_publish(qpool, x, w, ss, pos=p, rope=rope, bias=b, q_out=q_out, stream=stream)
+
+    def unfused():
+        qkv = torch.nn.functional.linear(x, w, b).view(n, 3, H, D)
+        qq = qkv[:, 0].contiguous()
+        wf.wf_kv_publish(qpool, qkv[:, 1], qkv[:, 2], ss, pos=p, rope=rope, q=qq, stream=stream)
+
+    def timed(fn):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        ms = []
+        for _ in range(steps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        return float(np.median(ms))
+
+    f_ms, u_ms = timed(fused), timed(unfused)
+    assert wf.wf_device_status() == 0
+    flops = 2.0 * n * hid * 3 * hid
+    tf = flops / (f_ms * 1e-3) / 1e12
+    return {"tokens": n, "hidden": hid, "fused_ms_p50": round(f_ms, 4),
+            "fused_tflops": round(tf, 2), "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+            "unfused_ms_p50": round(u_ms, 4), "kernel": "qkv_gemm_publish",
+            "unfused": "torch linear (library GEMM) + wf_kv_publish"}
+
+
 def time_history_rotate(cfg, torch, wf, reps: int = 200):
     """End-of-round history rotation (wf_history_rotate) on the page-aligned
     placement of the same context: average launch duration over `reps`
@@ -320,6 +370,7 @@ def main():
     }
     res["history_rotate"] = time_history_rotate(cfg, torch, wf)
     res["mx_variant"] = time_mx_variant(cfg, torch, wf, q, k, v, pos, pool, out, args.steps)
+    res["qkv_publish"] = time_qkv_publish(cfg, torch, wf, pos, args.steps)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
     print(json.dumps(res), flush=True)
