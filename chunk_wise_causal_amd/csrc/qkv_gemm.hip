@@ -20,7 +20,7 @@
 // (global_load_lds_dwordx4, two tiles ahead), 16-byte chunks XOR-swizzled by
 // row so that the fragment reads of 8 consecutive rows hit distinct banks;
 // one barrier per k-tile.  Blocks are dealt to the XCDs in contiguous runs,
-// and a run walks 8 token tiles per feature tile, so the blocks resident on
+// and a run walks 2 token tiles per feature tile, so the blocks resident on
 // one XCD share weight and hidden-state tiles in its L2.
 //
 // Epilogue per element: + bias, round to bf16 (the unfused projection's
@@ -39,7 +39,7 @@ constexpr int TN = 256;    // tokens per block
 constexpr int TK = 64;     // hidden elements per k-tile
 constexpr int NTH = 512;   // threads per block (8 waves)
 constexpr int NSL = 3;     // LDS ring slots
-constexpr int GT = 8;      // token tiles per feature tile in the block order
+constexpr int GT = 2;      // token tiles per feature tile in the block order
 constexpr int A_BYTES = TM * TK * 2;           // 16 KB
 constexpr int B_BYTES = TN * TK * 2;           // 32 KB
 constexpr int SLOT_BYTES = A_BYTES + B_BYTES;  // 48 KB
