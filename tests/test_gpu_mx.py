@@ -158,3 +158,45 @@ def test_full_size_14b_sampled():
     assert mx <= G.MAX_ABS and rr <= G.REL_RMS
     np.testing.assert_allclose(G.to_f64(lse)[heads][:, sel], l_ref[heads][:, sel], rtol=0,
                                atol=G.lse_atol("bf16"))
+
+
+def test_mx_segments_with_gaps_and_any_order():
+    """Segments in reverse order with gaps of never-written bytes (NaN codes)
+    between them: the 8-bit attention still reads only the named keys."""
+    cfg = medium(seed=46, page_size=64)
+    wl = make_workload(cfg)
+    c = wl.cfg
+    ref = oracle_layer(wl)
+    segs = c.segments()
+    new_segs, cursor = [], 0
+    for st, ln, slot in reversed(segs):
+        new_segs.append((cursor, ln, slot))
+        cursor += ln + 37
+    n_log = -(-cursor // c.page_size)
+    table = torch.randperm(n_log, generator=torch.Generator().manual_seed(4)).to(torch.int32)
+    pool = wf.KVPool.empty(n_log, c.heads, c.page_size, c.head_dim, table, device=G.DEV)
+    pool.v_pages.view(torch.int16).fill_(0x7FC1)
+    keys = wf.MXKeys.empty(n_log, c.heads, c.page_size, c.head_dim)
+    keys.codes.fill_(CODE_FILL)
+    keys.scales.fill_(SCALE_FILL)
+    k_rot = torch.from_numpy(ref["k_rot"].view(np.int16)).view(torch.bfloat16).to(G.DEV)
+    v = wl.v.to(G.DEV)
+    k8 = np.full((n_log, c.heads, c.page_size, c.head_dim), CODE_FILL, np.uint8)
+    k8s = np.full((n_log, c.heads, c.page_size, c.head_dim // 32), SCALE_FILL, np.uint8)
+    vp = np.full((n_log, c.heads, c.head_dim, c.page_size), 0x7FC1, np.uint16)
+    from oracle.publish import publish
+    for (st, ln, _), (nst, _, _) in zip(reversed(segs), new_segs):
+        wf.wf_kv_publish_mx(pool, keys, k_rot[st:st + ln], v[st:st + ln], nst)
+        mx_publish_keys(k8, k8s, table.numpy(), c.page_size, ref["k_rot"][st:st + ln], nst, "bf16")
+        publish(np.zeros((n_log, c.heads, c.page_size, c.head_dim), np.uint16), vp, table.numpy(),
+                c.page_size, ref["k_rot"][st:st + ln], ref["v"][st:st + ln], None, nst, "bf16")
+    q = wl.q.to(G.DEV)
+    out = wf.wf_chunk_attn_mx(pool, keys, new_segs, q, c.q_slot_start(), 0, c.scale)
+    torch.cuda.synchronize()
+    assert wf.wf_device_status() == 0
+    assert np.array_equal(keys.codes.cpu().numpy(), k8)
+    o_ref, _ = mx_chunk_attention(k8, k8s, vp, table.numpy(), c.page_size, new_segs, ref["q"],
+                                  c.q_slot_start(), 0, c.scale)
+    mx, rr = G.err_stats(G.to_f64(out), o_ref)
+    print(f"[mx] gaps/any order: max-abs {mx:.3e} rel-rms {rr:.3e}", flush=True)
+    assert mx <= G.MAX_ABS and rr <= G.REL_RMS
