@@ -152,7 +152,9 @@ __device__ __forceinline__ void mx_store(const PublishParams& p, void* k8_scales
 
 template <int D, typename T>
 union PublishShared {
-  static constexpr int VPAD = 16 / sizeof(T);   // LDS row padding (elements)
+  // LDS row padding (elements): 8 bytes, so that the 8 rows one run reads
+  // (8 apart) spread over more banks than with a 16-byte pad
+  static constexpr int VPAD = 8 / sizeof(T);
   float2 cs[kTileTok / 2][D / 2];               // K blocks: rotary factors (32 tokens)
   T vt[kTileTok][D + VPAD];                     // V blocks: staged rows
 };
@@ -296,8 +298,9 @@ __device__ __forceinline__ void v_block(
     const int L = L0 + ti;
     if (L < lo || L >= hi) continue;
     const int64_t t = L - p.dst_start;
-    *reinterpret_cast<uint4*>(&sm.vt[ti][c * EPV]) =
-        ld_stream(vin + t * p.v_stride + (int64_t)h * D + c * EPV);
+    const uint4 val = ld_stream(vin + t * p.v_stride + (int64_t)h * D + c * EPV);
+    reinterpret_cast<uint2*>(&sm.vt[ti][c * EPV])[0] = make_uint2(val.x, val.y);
+    reinterpret_cast<uint2*>(&sm.vt[ti][c * EPV])[1] = make_uint2(val.z, val.w);
   }
   __syncthreads();
 #pragma unroll
