@@ -288,13 +288,17 @@ int publish_impl(const wf_kv_pool* pool, const wf_mx_keys* mx, const wf_rope* ro
   p.num_logical_pages = pool->num_logical_pages;
   p.rope = rope ? 1 : 0;
   if (rope) fill_pairs(rope, p.pair_axis, p.pair_omega);
-  // 64-token tiles of the window; K blocks take up to 8 heads (the rotary
-  // factors of a tile are evaluated once per K block), V blocks one head
+  // 64-token tiles of the window; K blocks take groups of about 10 heads,
+  // split evenly (the rotary factors of a tile are evaluated once per K
+  // block), V blocks 256 features (bfloat16) or one head (float32)
   const int64_t tiles = ((int64_t)dst_logical_start + n_tok - 1) / 64 - dst_logical_start / 64 + 1;
   p.tiles = (int)tiles;
-  p.heads_per_kblock = std::min(pool->num_heads, 8);
-  const int64_t kgroups = (pool->num_heads + p.heads_per_kblock - 1) / p.heads_per_kblock;
-  const int64_t blocks = tiles * kgroups + tiles * pool->num_heads;
+  const int kgroups = (pool->num_heads + 9) / 10;
+  p.heads_per_kblock = (pool->num_heads + kgroups - 1) / kgroups;
+  const int64_t v_per_tile = (mx || pool->dtype == WF_BF16)
+                                 ? (pool->num_heads * pool->head_dim / 64 + 3) / 4
+                                 : pool->num_heads;
+  const int64_t blocks = tiles * kgroups + tiles * v_per_tile;
   if (blocks > 0x7fffffff) return fail(WF_ERR_UNSUPPORTED, "publish window too large");
   p.k_blocks = (int)(tiles * kgroups);
 

@@ -15,10 +15,12 @@
 //             multiply-add) -> round to the storage type -> 16-byte store
 //             into the K page row.  Registers are kept low (one head in
 //             flight per thread) so that six blocks share a CU.
-//   V blocks  (64-token tile x one head): rows staged in LDS, re-read by
-//             feature d and stored as runs of 8 consecutive tokens into the
-//             d-major V page (16-byte stores for bf16).  Thousands of small
-//             blocks keep enough bytes in flight.
+//   V blocks  (64-token tile x 256 features, bfloat16): every lane loads an
+//             8-token x 8-feature block, transposes it in registers and
+//             stores 8 runs of 8 consecutive tokens into the d-major V page
+//             (16-byte stores), with no LDS staging and no barrier before
+//             the stores.  For float32, a 64-token tile of one head is
+//             staged in LDS and re-read by feature.
 // Token tiles are aligned to 64 in logical space, so an 8-token run never
 // crosses a page (pages hold >= 16 tokens).
 #include <type_traits>
@@ -331,15 +333,82 @@ __device__ __forceinline__ void v_block(
   }
 }
 
+// V block without LDS (bfloat16): 64 tokens x 256 features (2 heads of 128
+// or 4 of 64).  Wave w takes a 64-feature block of one head; lane (c, g)
+// loads the 16-byte vectors c (features 8c..8c+7 of the block) of tokens
+// 8g..8g+7, transposes the 8 x 8 block in registers and stores 8 runs of 8
+// consecutive tokens, one per feature, into the d-major V page.
+template <int D>
+__device__ __forceinline__ void v_block_reg(const PublishParams& p, int tile, int vb,
+                                            int* page_of) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int fb = vb * (kThreads / 64) + wave;          // 64-feature block
+  const int h = fb / (D / 64), f0 = (fb % (D / 64)) * 64;
+  const int c = lane & 7, g = lane >> 3;
+  const int ps = 1 << p.ps_log2;
+  const int L0 = (p.dst_start / kTileTok + tile) * kTileTok;
+  const int lo = max(L0, p.dst_start);
+  const int hi = min(L0 + kTileTok, p.dst_start + p.n_tok);
+  const bool live = h < p.heads;
+  const uint16_t* __restrict__ vin = static_cast<const uint16_t*>(p.v);
+  uint16_t* __restrict__ vpg = static_cast<uint16_t*>(p.v_pages);
+  const int Lg = L0 + 8 * g;
+  uint4 r[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int L = Lg + j;
+    r[j] = make_uint4(0, 0, 0, 0);
+    if (live && L >= lo && L < hi)
+      r[j] = ld_stream(vin + (int64_t)(L - p.dst_start) * p.v_stride + (int64_t)h * D + f0 + 8 * c);
+  }
+  tile_pages(p, L0, lo, hi, page_of);
+  __syncthreads();
+  if (!live || Lg + 8 <= lo || Lg >= hi) return;
+  int page = -1;
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    if (Lg + e >= lo && Lg + e < hi) page = page_of[8 * g + e];
+  if (page < 0) return;
+  uint16_t* dst = vpg + (((int64_t)page * p.heads + h) * D + f0 + 8 * c) * ps + (Lg & (ps - 1));
+  const bool full = Lg >= lo && Lg + 8 <= hi;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    // run e: feature 8c+e of tokens 8g..8g+7 (element e of each r[j])
+    uint32_t w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t a = (&r[2 * k].x)[e >> 1], b = (&r[2 * k + 1].x)[e >> 1];
+      w[k] = (e & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
+    }
+    uint16_t* d = dst + (int64_t)e * ps;
+    if (full) {
+      st_stream(d, make_uint4(w[0], w[1], w[2], w[3]));
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (Lg + j >= lo && Lg + j < hi) d[j] = (uint16_t)(w[j >> 1] >> (16 * (j & 1)));
+    }
+  }
+}
+
+
 template <int D, bool BF16, bool HAS_Q, bool MX>
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(5)))
+// at least 5 waves per SIMD; the 8-bit variant that also rotates Q needs more
+// registers and takes 4
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
+                          amdgpu_waves_per_eu(MX && HAS_Q ? 4 : 5)))
 void publish_kernel(const PublishParams p, void* k8_scales) {
   using T = typename std::conditional<BF16, uint16_t, float>::type;
   __shared__ __attribute__((aligned(16))) PublishShared<D, T> sm;
   __shared__ int page_of[kTileTok];
   const int b = blockIdx.x;
-  if (b < p.k_blocks) k_block<D, BF16, HAS_Q, MX>(p, k8_scales, b, sm, page_of);
-  else v_block<D, BF16>(p, b - p.k_blocks, sm, page_of);
+  if (b < p.k_blocks) {
+    k_block<D, BF16, HAS_Q, MX>(p, k8_scales, b, sm, page_of);
+  } else {
+    const int vb = b - p.k_blocks;
+    if constexpr (BF16) v_block_reg<D>(p, vb % p.tiles, vb / p.tiles, page_of);
+    else v_block<D, BF16>(p, vb, sm, page_of);
+  }
 }
 
 template <int D, bool BF16>
@@ -353,8 +422,14 @@ void launch_typed(const PublishParams& p, dim3 grid, dim3 block, hipStream_t str
 
 }  // namespace
 
+// V blocks per 64-token tile: bfloat16 blocks take 256 features (4 waves of
+// 64), float32 blocks one head
+int v_blocks_per_tile(const PublishParams& p, bool bf16) {
+  return bf16 ? (p.heads * p.head_dim / 64 + 3) / 4 : p.heads;
+}
+
 hipError_t launch_publish_mx(const PublishParams& p, void* k8_scales, hipStream_t stream) {
-  const int v_blocks = p.tiles * p.heads;
+  const int v_blocks = p.tiles * v_blocks_per_tile(p, true);
   dim3 grid(p.k_blocks + v_blocks), block(kThreads);
   if (p.q)
     hipLaunchKernelGGL((publish_kernel<128, true, true, true>), grid, block, 0, stream, p,
@@ -366,9 +441,9 @@ hipError_t launch_publish_mx(const PublishParams& p, void* k8_scales, hipStream_
 }
 
 hipError_t launch_publish(const PublishParams& p, int dtype, hipStream_t stream) {
-  const int v_blocks = p.tiles * p.heads;
-  dim3 grid(p.k_blocks + v_blocks), block(kThreads);
   const bool bf16 = dtype == WF_BF16;
+  const int v_blocks = p.tiles * v_blocks_per_tile(p, bf16);
+  dim3 grid(p.k_blocks + v_blocks), block(kThreads);
   if (p.head_dim == 128) {
     if (bf16) launch_typed<128, true>(p, grid, block, stream);
     else launch_typed<128, false>(p, grid, block, stream);
