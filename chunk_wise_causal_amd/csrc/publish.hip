@@ -14,7 +14,7 @@
 //             16-byte vector load -> rotate pairs in float (no fused
 //             multiply-add) -> round to the storage type -> 16-byte store
 //             into the K page row.  Registers are kept low (one head in
-//             flight per thread) so that six blocks share a CU.
+//             flight per thread) so that several blocks share a CU.
 //   V blocks  (64-token tile x 256 features, bfloat16): every lane loads an
 //             8-token x 8-feature block, transposes it in registers and
 //             stores 8 runs of 8 consecutive tokens into the d-major V page
@@ -391,10 +391,9 @@ __device__ __forceinline__ void v_block_reg(const PublishParams& p, int tile, in
   }
 }
 
-
-template <int D, bool BF16, bool HAS_Q, bool MX>
 // at least 5 waves per SIMD; the 8-bit variant that also rotates Q needs more
 // registers and takes 4
+template <int D, bool BF16, bool HAS_Q, bool MX>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                           amdgpu_waves_per_eu(MX && HAS_Q ? 4 : 5)))
 void publish_kernel(const PublishParams p, void* k8_scales) {
@@ -424,7 +423,7 @@ void launch_typed(const PublishParams& p, dim3 grid, dim3 block, hipStream_t str
 
 // V blocks per 64-token tile: bfloat16 blocks take 256 features (4 waves of
 // 64), float32 blocks one head
-int v_blocks_per_tile(const PublishParams& p, bool bf16) {
+static int v_blocks_per_tile(const PublishParams& p, bool bf16) {
   return bf16 ? (p.heads * p.head_dim / 64 + 3) / 4 : p.heads;
 }
 
