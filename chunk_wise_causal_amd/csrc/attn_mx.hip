@@ -719,10 +719,8 @@ void attn_fwd_mx(const AttnParams p, const uint8_t* k8_scales) {
   const int lane = tid & 63, wave = tid >> 6;
   const int ql = lane & 31, hg = lane >> 5;
 
-  // ---- work item: XCD-contiguous remap of the block id --------------------
-  const int nb = gridDim.x, b = blockIdx.x;
-  const int per = nb >> 3;
-  const int w = (b < (per << 3)) ? ((b & 7) * per + (b >> 3)) : b;
+  // ---- work item: XCD-contiguous runs, longest first within each --------
+  const int w = xcd_work_item(p, blockIdx.x, gridDim.x);
   const int head = w / p.tiles_per_head;
   const int tw = w - head * p.tiles_per_head;
   int grp = 0;

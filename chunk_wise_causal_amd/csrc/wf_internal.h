@@ -59,6 +59,33 @@ struct AttnParams {
   int2 ranges[kMaxRanges];           // [lo, hi) logical key ranges, sorted
 };
 
+// Work item (index into the head-major list of (head, group, query tile))
+// of attention block b of nb.  The hardware deals blocks round-robin to the
+// 8 XCDs, so XCD x runs blocks x, x+8, ...  It is given the contiguous run
+// [x*per, (x+1)*per) of the list, which keeps the query tiles of a head on
+// one XCD and its key/value tiles in that XCD's L2.  Within the run the
+// items go longest first: group by group in work order (longest visible
+// context first), head by head, tile by tile, so the XCD's last blocks are
+// its shortest.  Blocks past 8*per keep their own index.
+__device__ __forceinline__ int xcd_work_item(const AttnParams& p, int b, int nb) {
+  const int per = nb >> 3;
+  if (b >= (per << 3)) return b;
+  const int r0 = (b & 7) * per, r1 = r0 + per;
+  const int T = p.tiles_per_head;
+  const int h_lo = r0 / T, h_hi = (r1 - 1) / T;
+  int k = b >> 3;
+  for (int g = 0; g < p.n_groups; ++g) {
+    const int gs = g ? p.grp_tile_end[g - 1] : 0, ge = p.grp_tile_end[g];
+    for (int hd = h_lo; hd <= h_hi; ++hd) {
+      const int lo = max(hd * T + gs, r0), hi = min(hd * T + ge, r1);
+      const int cnt = max(hi - lo, 0);
+      if (k < cnt) return lo + k;
+      k -= cnt;
+    }
+  }
+  return r0 + k;   // not reached: the run holds per items
+}
+
 // launches (stream-ordered; return hipError_t of the launch)
 hipError_t launch_publish(const PublishParams& p, int dtype, hipStream_t stream);
 hipError_t launch_attn_bf16(const AttnParams& p, int head_dim, int block_m,
