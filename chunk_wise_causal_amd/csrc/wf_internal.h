@@ -59,15 +59,17 @@ struct AttnParams {
   int2 ranges[kMaxRanges];           // [lo, hi) logical key ranges, sorted
 };
 
-// Work item (index into the head-major list of (head, group, query tile))
-// of attention block b of nb.  The hardware deals blocks round-robin to the
-// 8 XCDs, so XCD x runs blocks x, x+8, ...  It is given the contiguous run
-// [x*per, (x+1)*per) of the list, which keeps the query tiles of a head on
-// one XCD and its key/value tiles in that XCD's L2.  Within the run the
-// items go longest first: group by group in work order (longest visible
-// context first), head by head, tile by tile, so the XCD's last blocks are
-// its shortest.  Blocks past 8*per keep their own index.
-__device__ __forceinline__ int xcd_work_item(const AttnParams& p, int b, int nb) {
+// Work items of the attention blocks.  An item is an index into the
+// head-major list of (head, group, query tile).  The hardware deals blocks
+// round-robin to the 8 XCDs, so XCD x runs blocks x, x+8, ... (n_x of them:
+// nb/8, plus one for x < nb%8), in that order.
+//
+// xcd_run_item: XCD x takes the contiguous run [x*per, (x+1)*per) of the
+// list (per = nb/8), which keeps the query tiles of a head on one XCD and
+// its key/value tiles in that XCD's L2; within the run the items go longest
+// first (group by group in work order, head by head, tile by tile).  Blocks
+// past 8*per keep their own index.
+__host__ __device__ __forceinline__ int xcd_run_item(const AttnParams& p, int b, int nb) {
   const int per = nb >> 3;
   if (b >= (per << 3)) return b;
   const int r0 = (b & 7) * per, r1 = r0 + per;
@@ -84,6 +86,55 @@ __device__ __forceinline__ int xcd_work_item(const AttnParams& p, int b, int nb)
     }
   }
   return r0 + k;   // not reached: the run holds per items
+}
+
+// Items of group g (all heads) and XCD x's share of them: an eighth of every
+// group but the last, contiguous in head-major order; the last (shortest)
+// group fills the XCD up to its n_x blocks.
+__host__ __device__ __forceinline__ int64_t group_items(const AttnParams& p, int g) {
+  return (int64_t)(p.grp_tile_end[g] - (g ? p.grp_tile_end[g - 1] : 0)) * p.heads;
+}
+__host__ __device__ __forceinline__ int group_share(const AttnParams& p, int g, int x) {
+  const int64_t n = group_items(p, g);
+  return (int)((((int64_t)x + 1) * n >> 3) - (((int64_t)x * n) >> 3));
+}
+__host__ __device__ __forceinline__ int last_group_share(const AttnParams& p, int nb, int x) {
+  int s = (nb >> 3) + (x < (nb & 7) ? 1 : 0);
+  for (int g = 0; g + 1 < p.n_groups; ++g) s -= group_share(p, g, x);
+  return s;
+}
+
+// xcd_work_item: every XCD takes its share of every group, groups in work
+// order (longest visible context first), each share contiguous in
+// head-major order (a few heads' tiles, whose key/value tiles stay in the
+// XCD's L2).  Every XCD thus gets the same mix of long and short items,
+// longest first.  When the last group is too small to even out the counts
+// (tiny grids), the runs of xcd_run_item are used instead.
+__host__ __device__ __forceinline__ int xcd_work_item(const AttnParams& p, int b, int nb) {
+  const int G = p.n_groups;
+  for (int x = 0; x < 8; ++x)
+    if (last_group_share(p, nb, x) < 0) return xcd_run_item(p, b, nb);
+  const int x = b & 7;
+  int k = b >> 3;
+  for (int g = 0; g < G; ++g) {
+    const bool last = g + 1 == G;
+    const int s = last ? last_group_share(p, nb, x) : group_share(p, g, x);
+    if (k < s) {
+      int o = 0;
+      if (!last) {
+        o = (int)(((int64_t)x * group_items(p, g)) >> 3);
+      } else {
+        for (int xx = 0; xx < x; ++xx) o += last_group_share(p, nb, xx);
+      }
+      const int j = o + k;
+      const int gs = g ? p.grp_tile_end[g - 1] : 0;
+      const int tg = p.grp_tile_end[g] - gs;
+      const int head = j / tg;
+      return head * p.tiles_per_head + gs + (j - head * tg);
+    }
+    k -= s;
+  }
+  return b;   // not reached: the shares hold every block
 }
 
 // launches (stream-ordered; return hipError_t of the launch)
