@@ -2,7 +2,7 @@
 
     python -m chunk_wise_causal_amd.build          # or __graft_entry__.build()
 
-Always recompiles.  Flags: -O3, C++17, position-independent shared library,
+Always recompiles (the sources in parallel).  Flags: -O3, C++17, position-independent shared library,
 and packed FP32 instructions disabled on the device (hipcc's host pass warns
 that it does not know that target feature; the warning is harmless).
 """
@@ -11,6 +11,7 @@ from __future__ import annotations
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
@@ -31,16 +32,21 @@ def hipcc() -> str:
     return path if os.path.exists(path) else "hipcc"
 
 
-def build(verbose: bool = False) -> str:
-    objs = []
+def build(verbose: bool = False, jobs: int = 0) -> str:
+    """Compile every source (in parallel, `jobs` at a time; 0: one per CPU,
+    at most 8) and link libwf.so."""
     build_dir = os.path.join(HERE, "_build")
     os.makedirs(build_dir, exist_ok=True)
-    for src in SOURCES:
+
+    def compile_one(src):
         obj = os.path.join(build_dir, src + ".o")
         lang = ["-x", "hip"] if src.endswith(".cpp") else []
-        cmd = [hipcc(), *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
-        _run(cmd, verbose)
-        objs.append(obj)
+        _run([hipcc(), *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
+        return obj
+
+    workers = jobs or max(1, min(8, os.cpu_count() or 1))
+    with ThreadPoolExecutor(max_workers=workers) as pool:
+        objs = list(pool.map(compile_one, SOURCES))
     tmp = LIB + ".tmp"
     _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
