@@ -89,7 +89,7 @@ def copy_calibration(torch):
 def traffic_from_profiles(kernel_src_hash: str):
     """HBM bytes per attention launch from the committed counter summary, or
     None when it is missing or was taken on other kernel sources."""
-    path = os.path.join(ROOT, "profiles", "attn_fwd_bf16_cfg4_traffic.json")
+    path = os.path.join(ROOT, "profiles", "attn_fwd_bf16_14b_4step_traffic.json")
     try:
         with open(path) as f:
             d = json.load(f)
@@ -347,7 +347,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic: Q/K/V ~ N(0,1) bf16 drawn on device, seeded; random-permuted pages",
-        "config": {"workload": f"layer tick, cfg{args.config}: {cfg.name}",
+        "config": {"workload": f"layer tick: {cfg.name}",
                    "heads": cfg.heads, "head_dim": cfg.head_dim, "chunk": cfg.chunk,
                    "anchor": cfg.anchor_tokens, "history_chunks": cfg.n_hist,
                    "slots": cfg.slots, "n_q": cfg.n_q, "n_kv": cfg.n_kv,

@@ -3,7 +3,8 @@
 bfloat16 is kept as uint16 bit patterns: the upper half of an IEEE binary32.
 Upcasting is exact.  Downcasting rounds to nearest, ties to even, which is the
 rounding the rotary embedding's output uses ([WF] §4.2 publishes RoPE'd K in
-the model's storage type; the rounding rule is this build's stated reading).
+the model's storage type; the pages do not name the rounding, and round to
+nearest even is the reading taken).
 """
 from __future__ import annotations
 

@@ -36,7 +36,7 @@ def medium(**kw):
 
 
 SHAPES = {
-    "cfg1_fp32": CONFIGS[1],
+    "tiny_fp32": CONFIGS[1],
     "small_ps16": small_config(),
     "medium_ps64": medium(),
     "medium_ps256_stale": medium(page_size=256, stale_frac=0.1, seed=22),

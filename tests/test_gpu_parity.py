@@ -35,7 +35,7 @@ def medium(**kw):
 
 
 SHAPES = {
-    "cfg1_fp32": CONFIGS[1],
+    "tiny_fp32": CONFIGS[1],
     "small_ps16": small_config(),
     "small_d64_ps32": small_config(head_dim=64, rope=(24, 20, 20), page_size=32, seed=12),
     "medium_ps64": medium(),

@@ -50,7 +50,7 @@ def test_single_slot_is_dense_attention(prefix):
     np.testing.assert_allclose(lse, l_ref.numpy(), rtol=0, atol=1e-11)
 
 
-@pytest.mark.parametrize("cfg", [CONFIGS[1], small_config()], ids=["cfg1_fp32", "small_bf16"])
+@pytest.mark.parametrize("cfg", [CONFIGS[1], small_config()], ids=["tiny_fp32", "small_bf16"])
 def test_matches_brute_force(cfg):
     wl = make_workload(cfg)
     ref = oracle_layer(wl)
@@ -224,7 +224,7 @@ def _gattn(wl, ref, runs, groups):
                            groups, ref["q"], c.scale, c.dtype)
 
 
-@pytest.mark.parametrize("cfg", [CONFIGS[1], small_config(slots=2)], ids=["cfg1_fp32", "small_bf16"])
+@pytest.mark.parametrize("cfg", [CONFIGS[1], small_config(slots=2)], ids=["tiny_fp32", "small_bf16"])
 def test_group_attention_matches_brute_force(cfg):
     wl = make_workload(cfg)
     ref = oracle_layer(wl)

@@ -85,7 +85,7 @@ def test_q_rotated_like_k():
 
 
 def test_stale_pages_untouched_by_layer_publish():
-    """cfg3-style pool: 10% extra physical pages hold stale N(0,4) data that
+    """A pool like the 1.3B-like 5-step one: 10% extra physical pages hold stale N(0,4) data that
     no publish may write (and no visible key maps to)."""
     cfg = small_config(stale_frac=0.25, page_size=16)
     wl = make_workload(cfg)
