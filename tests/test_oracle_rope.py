@@ -127,3 +127,98 @@ def test_float32_path_tracks_float64():
     y32 = rotate_f32(x, pos, (44, 42, 42), 1e4).astype(np.float64)
     y64 = rotate_f64(x.astype(np.float64), pos, (44, 42, 42), 1e4)
     np.testing.assert_allclose(y32, y64, rtol=0, atol=3e-6)
+
+
+# ---- the rounding rule of the rotation (R9) --------------------------------
+# The precision reading of the publish (K rotated before publishing, "Wave
+# Forcing", §4.2): cos and sin rounded to float32, then
+#   y0 = f32(f32(x0*c) - f32(x1*s)),   y1 = f32(f32(x0*s) + f32(x1*c)),
+# each product and the sum rounded on its own (no fused multiply-add), then
+# round-to-nearest-even to the storage type.  Hand-worked cases at the 1 rad
+# angle of the closed-form table (split 24/20/20, pair 27, w position 100;
+# c = f32(cos 1) = 0x3f0a5140, s = f32(sin 1) = 0x3f576aa4), with inputs
+# chosen so that the per-operation result, the single-rounding result
+# f32(x0*c - x1*s) and the fused result f32(x0*c - f32(x1*s)) all differ.
+# Each row: output (0: y0, 1: y1), x0 bits, x1 bits, then the per-operation
+# float32 bits (the reading), the single-rounding and fused float32 bits, and
+# the bfloat16 bits of the reading and of the single rounding.  The float32
+# values were worked out with exact rational arithmetic and explicit
+# round-to-nearest-even; test_rounding_cases_are_exact re-derives them.
+R9_CASES = [
+    # y0 = x0*c - x1*s
+    (0, 0xbf887961, 0xbf2d7ae9, 0xbbbf8000, 0xbbbf7ff5, 0xbbbf7fd0, 0xbbc0, 0xbbbf),
+    (0, 0x3f116cee, 0x3eb9bbfd, 0x3adb8000, 0x3adb7fef, 0x3adb803d, 0x3adc, 0x3adb),
+    # y1 = x0*s + x1*c
+    (1, 0x3f241f3e, 0xbf7e7582, 0x3b1e8000, 0x3b1e8046, 0x3b1e8026, 0x3b1e, 0x3b1f),
+    (1, 0xbf2db598, 0x3f86c2a0, 0xbb0c8000, 0xbb0c8017, 0xbb0c8021, 0xbb0c, 0xbb0d),
+    (1, 0xbf9c7a40, 0x3ff3727d, 0xba8b8000, 0xba8b7c93, 0xba8b7e73, 0xba8c, 0xba8b),
+]
+R9_C, R9_S = 0x3f0a5140, 0x3f576aa4
+
+
+def _f32(bits):
+    return np.array([bits], dtype=np.uint32).view(np.float32)[0]
+
+
+def _bits(x):
+    return int(np.array([x], dtype=np.float32).view(np.uint32)[0])
+
+
+def _rne(fr, mant_bits):
+    """Round a nonzero rational to `mant_bits` significand bits, ties to even
+    (normal range)."""
+    from fractions import Fraction
+    sign = -1 if fr < 0 else 1
+    a = abs(fr)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    ulp = Fraction(2) ** (e - (mant_bits - 1))
+    q = a / ulp
+    n, rem = divmod(q.numerator, q.denominator)
+    rem = Fraction(rem, q.denominator)
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    return sign * n * ulp
+
+
+def test_rounding_factors_of_the_case_angle():
+    # the 1 rad factors of the case table, rounded from double precision
+    assert _bits(np.float32(COS[1.0])) == R9_C and _bits(np.float32(SIN[1.0])) == R9_S
+    from oracle.rope import pair_factors
+    c, s = pair_factors(np.array([[0, 0, 100]]), (24, 20, 20), 10000.0)
+    assert _bits(c[0, 27]) == R9_C and _bits(s[0, 27]) == R9_S
+
+
+@pytest.mark.parametrize("case", R9_CASES)
+def test_rounding_cases_are_exact(case):
+    from fractions import Fraction as Fr
+    out, bx0, bx1, per_op, single, fused, bf_per_op, bf_single = case
+    x0, x1 = Fr(float(_f32(bx0))), Fr(float(_f32(bx1)))
+    c, s = Fr(float(_f32(R9_C))), Fr(float(_f32(R9_S)))
+    if out == 0:
+        a, b, sign = x0 * c, x1 * s, -1
+    else:
+        a, b, sign = x0 * s, x1 * c, 1
+    r = _rne(_rne(a, 24) + sign * _rne(b, 24), 24)
+    assert _bits(float(r)) == per_op
+    assert _bits(float(_rne(a + sign * b, 24))) == single
+    assert _bits(float(_rne(a + sign * _rne(b, 24), 24))) == fused
+    assert _bits(float(_rne(r, 8))) >> 16 == bf_per_op
+    assert _bits(float(_rne(_rne(a + sign * b, 24), 8))) >> 16 == bf_single
+    # the three readings are distinguishable on these inputs
+    assert len({per_op, single, fused}) == 3 and bf_per_op != bf_single
+
+
+@pytest.mark.parametrize("case", R9_CASES)
+def test_rotation_rounds_every_operation(case):
+    out, bx0, bx1, per_op, _, _, bf_per_op, _ = case
+    split, p, pos = (24, 20, 20), 27, np.array([[0, 0, 100]], dtype=np.int32)
+    x = np.zeros((1, 1, 64), dtype=np.float32)
+    x[0, 0, 2 * p], x[0, 0, 2 * p + 1] = _f32(bx0), _f32(bx1)
+    y = rotate_f32(x, pos, split, 10000.0)[0, 0, 2 * p + out]
+    assert _bits(y) == per_op
+    yb = apply_rope(x, pos, split, 10000.0, "bf16")[0, 0, 2 * p + out]
+    assert int(np.asarray(yb).view(np.uint16)) == bf_per_op
