@@ -127,6 +127,63 @@ def _row_stride(t: torch.Tensor, name: str) -> int:
     return t.stride(0)
 
 
+# ---- argument checks the C side cannot make --------------------------------
+# The library sees raw pointers: it checks strides, alignment and NULLs, but
+# not where a buffer lives, its element type or how many rows it holds.  These
+# checks run before any library call, so a bad argument raises ValueError
+# instead of sending a host pointer or a short buffer to a kernel.  Shape and
+# type checks come first, the device check last.
+
+def _on_device(t: torch.Tensor, dev: torch.device, name: str) -> None:
+    if not t.is_cuda or t.device != dev:
+        raise ValueError(f"{name}: must be a GPU tensor on {dev}, got {t.device}")
+
+
+def _pool_device(pool: "KVPool") -> torch.device:
+    dev = pool.k_pages.device
+    if not pool.k_pages.is_cuda:
+        raise ValueError(f"pool: page arrays must be GPU tensors, got {dev}")
+    for t, name in ((pool.v_pages, "pool.v_pages"), (pool.page_table, "pool.page_table")):
+        _on_device(t, dev, name)
+    return dev
+
+
+def _head_rows(pool: "KVPool", t: torch.Tensor, name: str, rows: int) -> int:
+    """t is [>= rows, H, D] of the pool's element type with contiguous rows;
+    returns its row stride (elements)."""
+    H, D = pool.desc.num_heads, pool.desc.head_dim
+    if t.dim() != 3 or tuple(t.shape[1:]) != (H, D):
+        raise ValueError(f"{name}: expected [rows, {H}, {D}], got {list(t.shape)}")
+    if t.dtype != pool.k_pages.dtype:
+        raise ValueError(f"{name}: dtype {t.dtype} differs from the pool's {pool.k_pages.dtype}")
+    if t.shape[0] < rows:
+        raise ValueError(f"{name}: {t.shape[0]} rows, the call reads or writes {rows}")
+    return _row_stride(t, name)
+
+
+def _positions(pos: Optional[torch.Tensor], n: int, rope) -> None:
+    if pos is None:
+        if rope is not None and n > 0:
+            raise ValueError("pos: required with rope")
+        return
+    if pos.dtype != torch.int32 or not pos.is_contiguous() or tuple(pos.shape) != (n, 3):
+        raise ValueError(f"pos must be a contiguous int32 [{n}, 3] tensor, got "
+                         f"{pos.dtype} {list(pos.shape)}")
+
+
+def _lse(lse: torch.Tensor, H: int, rows: int, exact: bool) -> int:
+    """lse is float32 [H, n] with contiguous rows and n == rows (exact) or
+    n >= rows; returns its row stride."""
+    if lse.dim() != 2 or lse.dtype != torch.float32 or lse.stride(1) != 1:
+        raise ValueError("lse: expected [heads, n] float32 with contiguous rows")
+    if lse.shape[0] != H or (lse.shape[1] != rows if exact else lse.shape[1] < rows):
+        want = f"[{H}, {rows}]" if exact else f"[{H}, >= {rows}]"
+        raise ValueError(f"lse: expected {want}, got {list(lse.shape)}")
+    if exact and lse.stride(0) != rows:
+        raise ValueError("lse: expected a contiguous [heads, rows] tensor")
+    return lse.stride(0)
+
+
 class KVPool:
     """A paged K/V pool in device memory (layout of include/wf.h):
     k_pages [num_pages, H, page_size, D], v_pages [num_pages, H, D, page_size]
@@ -166,16 +223,19 @@ def wf_kv_publish(pool: KVPool, k: torch.Tensor, v: torch.Tensor, dst_start: int
                   q: Optional[torch.Tensor] = None, stream=None) -> None:
     """RoPE K (and q, in place) with `pos` and scatter K, V into the pool at
     logical rows dst_start.. (C: wf_kv_publish)."""
-    n = k.shape[0]
+    n = k.shape[0] if k.dim() > 0 else 0
+    ks = _head_rows(pool, k, "k", n)
+    vs = _head_rows(pool, v, "v", n)
+    qs = _head_rows(pool, q, "q", n) if q is not None else 0
+    _positions(pos, n, rope)
+    dev = _pool_device(pool)
+    for t, name in ((k, "k"), (v, "v"), (q, "q"), (pos, "pos")):
+        if t is not None:
+            _on_device(t, dev, name)
     r = None
     if rope is not None:
         (dt, dh, dw), theta = rope
         r = wf_rope(dt, dh, dw, float(theta))
-    ks = _row_stride(k, "k")
-    vs = _row_stride(v, "v")
-    qs = _row_stride(q, "q") if q is not None else 0
-    if pos is not None and (pos.dtype != torch.int32 or not pos.is_contiguous()):
-        raise ValueError("pos must be a contiguous int32 [n, 3] tensor")
     rc = lib().wf_kv_publish(ctypes.byref(pool.desc), ctypes.byref(r) if r else None,
                              _ptr(k), ks, _ptr(v), vs, _ptr(pos), n, dst_start,
                              _ptr(q), qs, _stream(stream))
@@ -187,17 +247,26 @@ def wf_chunk_attn(pool: KVPool, segments: Sequence[Tuple[int, int, int]], q: tor
                   scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
                   lse: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """Chunk-wise causal attention of the query slots over the pool
-    (C: wf_chunk_attn).  Returns `out` ([rows, H, D], allocated if None)."""
+    (C: wf_chunk_attn).  Returns `out` ([rows, H, D], allocated if None);
+    lse, if given, is float32 [H, q_slot_start[-1]]."""
+    rows = int(q_slot_start[-1]) if len(q_slot_start) else 0
+    qs = _head_rows(pool, q, "q", rows)
     if out is None:
         out = torch.empty_like(q)
+    os_ = _head_rows(pool, out, "out", rows)
+    if lse is not None:
+        _lse(lse, pool.desc.num_heads, rows, exact=True)
+    dev = _pool_device(pool)
+    for t, name in ((q, "q"), (out, "out"), (lse, "lse")):
+        if t is not None:
+            _on_device(t, dev, name)
     if scale is None:
         scale = 1.0 / math.sqrt(q.shape[-1])
     segs = (wf_segment * len(segments))(*[wf_segment(*s) for s in segments])
     qss = (ctypes.c_int32 * len(q_slot_start))(*q_slot_start)
-    rc = lib().wf_chunk_attn(ctypes.byref(pool.desc), segs, len(segments), _ptr(q),
-                             _row_stride(q, "q"), qss, len(q_slot_start) - 1, first_slot,
-                             float(scale), _ptr(out), _row_stride(out, "out"), _ptr(lse),
-                             _stream(stream))
+    rc = lib().wf_chunk_attn(ctypes.byref(pool.desc), segs, len(segments), _ptr(q), qs, qss,
+                             len(q_slot_start) - 1, first_slot, float(scale), _ptr(out), os_,
+                             _ptr(lse), _stream(stream))
     _check(rc)
     return out
 
@@ -210,20 +279,23 @@ def wf_group_attn(pool: KVPool, runs: Sequence[Tuple[int, int]],
     runs: (kv_start, kv_len); groups: (q_row_start, q_row_end, run_begin,
     run_end).  lse, if given, is [H, n] float32 with n >= every q_row_end.
     Returns `out` ([rows, H, D], allocated if None)."""
+    rows = max([int(g[1]) for g in groups], default=0)
+    qs = _head_rows(pool, q, "q", rows)
     if out is None:
         out = torch.empty_like(q)
+    os_ = _head_rows(pool, out, "out", rows)
+    lse_stride = _lse(lse, pool.desc.num_heads, rows, exact=False) if lse is not None else 0
+    dev = _pool_device(pool)
+    for t, name in ((q, "q"), (out, "out"), (lse, "lse")):
+        if t is not None:
+            _on_device(t, dev, name)
     if scale is None:
         scale = 1.0 / math.sqrt(q.shape[-1])
     rs = (wf_kv_run * len(runs))(*[wf_kv_run(*r) for r in runs])
     gs = (wf_query_group * len(groups))(*[wf_query_group(*g) for g in groups])
-    lse_stride = 0
-    if lse is not None:
-        if lse.dim() != 2 or lse.dtype != torch.float32 or lse.stride(1) != 1:
-            raise ValueError("lse: expected [heads, n] float32 with contiguous rows")
-        lse_stride = lse.stride(0)
     rc = lib().wf_group_attn(ctypes.byref(pool.desc), rs, len(runs), gs, len(groups), _ptr(q),
-                             _row_stride(q, "q"), float(scale), _ptr(out),
-                             _row_stride(out, "out"), _ptr(lse), lse_stride, _stream(stream))
+                             qs, float(scale), _ptr(out), os_, _ptr(lse), lse_stride,
+                             _stream(stream))
     _check(rc)
     return out
 
@@ -252,23 +324,40 @@ class MXKeys:
                                device=device))
 
 
+def _mx_shape(keys: "MXKeys", pool: KVPool) -> None:
+    if tuple(keys.codes.shape) != (pool.desc.num_pages, pool.desc.num_heads,
+                                   pool.desc.page_size, pool.desc.head_dim):
+        raise ValueError("MX keys: codes must be [num_pages, H, page_size, head_dim] of the pool")
+
+
+def _mx_device(keys: "MXKeys", dev: torch.device) -> None:
+    _on_device(keys.codes, dev, "keys.codes")
+    _on_device(keys.scales, dev, "keys.scales")
+
+
 def wf_kv_publish_mx(pool: KVPool, keys: MXKeys, k: torch.Tensor, v: torch.Tensor,
                      dst_start: int, pos: Optional[torch.Tensor] = None,
                      rope: Optional[Tuple[Tuple[int, int, int], float]] = None,
                      q: Optional[torch.Tensor] = None, stream=None) -> None:
     """wf_kv_publish with K quantized to MXFP8 into `keys` (C: wf_kv_publish_mx)."""
-    n = k.shape[0]
+    n = k.shape[0] if k.dim() > 0 else 0
+    ks = _head_rows(pool, k, "k", n)
+    vs = _head_rows(pool, v, "v", n)
+    qs = _head_rows(pool, q, "q", n) if q is not None else 0
+    _positions(pos, n, rope)
+    _mx_shape(keys, pool)
+    dev = _pool_device(pool)
+    _mx_device(keys, dev)
+    for t, name in ((k, "k"), (v, "v"), (q, "q"), (pos, "pos")):
+        if t is not None:
+            _on_device(t, dev, name)
     r = None
     if rope is not None:
         (dt, dh, dw), theta = rope
         r = wf_rope(dt, dh, dw, float(theta))
-    qs = _row_stride(q, "q") if q is not None else 0
-    if pos is not None and (pos.dtype != torch.int32 or not pos.is_contiguous()):
-        raise ValueError("pos must be a contiguous int32 [n, 3] tensor")
     rc = lib().wf_kv_publish_mx(ctypes.byref(pool.desc), ctypes.byref(keys.desc),
-                                ctypes.byref(r) if r else None, _ptr(k), _row_stride(k, "k"),
-                                _ptr(v), _row_stride(v, "v"), _ptr(pos), n, dst_start, _ptr(q),
-                                qs, _stream(stream))
+                                ctypes.byref(r) if r else None, _ptr(k), ks, _ptr(v), vs,
+                                _ptr(pos), n, dst_start, _ptr(q), qs, _stream(stream))
     _check(rc)
 
 
@@ -277,16 +366,27 @@ def wf_chunk_attn_mx(pool: KVPool, keys: MXKeys, segments: Sequence[Tuple[int, i
                      scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
                      lse: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """Chunk-wise causal attention with the 8-bit QK^T (C: wf_chunk_attn_mx)."""
+    rows = int(q_slot_start[-1]) if len(q_slot_start) else 0
+    qs = _head_rows(pool, q, "q", rows)
     if out is None:
         out = torch.empty_like(q)
+    os_ = _head_rows(pool, out, "out", rows)
+    if lse is not None:
+        _lse(lse, pool.desc.num_heads, rows, exact=True)
+    _mx_shape(keys, pool)
+    dev = _pool_device(pool)
+    _mx_device(keys, dev)
+    for t, name in ((q, "q"), (out, "out"), (lse, "lse")):
+        if t is not None:
+            _on_device(t, dev, name)
     if scale is None:
         scale = 1.0 / math.sqrt(q.shape[-1])
     segs = (wf_segment * len(segments))(*[wf_segment(*s) for s in segments])
     qss = (ctypes.c_int32 * len(q_slot_start))(*q_slot_start)
     rc = lib().wf_chunk_attn_mx(ctypes.byref(pool.desc), ctypes.byref(keys.desc), segs,
-                                len(segments), _ptr(q), _row_stride(q, "q"), qss,
-                                len(q_slot_start) - 1, first_slot, float(scale), _ptr(out),
-                                _row_stride(out, "out"), _ptr(lse), _stream(stream))
+                                len(segments), _ptr(q), qs, qss, len(q_slot_start) - 1,
+                                first_slot, float(scale), _ptr(out), os_, _ptr(lse),
+                                _stream(stream))
     _check(rc)
     return out
 
@@ -301,18 +401,28 @@ def wf_qkv_publish(pool: KVPool, x: torch.Tensor, w_qkv: torch.Tensor, dst_start
     if given (C: wf_qkv_publish)."""
     if x.dim() != 2 or x.stride(1) != 1 or w_qkv.dim() != 2 or not w_qkv.is_contiguous():
         raise ValueError("x: [n, hidden] with contiguous rows; w_qkv: contiguous [3*H*D, hidden]")
-    if bias is not None and not bias.is_contiguous():
-        raise ValueError("bias must be contiguous")
-    if pos is not None and (pos.dtype != torch.int32 or not pos.is_contiguous()):
-        raise ValueError("pos must be a contiguous int32 [n, 3] tensor")
+    n, hidden = x.shape
+    F = 3 * pool.desc.num_heads * pool.desc.head_dim
+    if tuple(w_qkv.shape) != (F, hidden):
+        raise ValueError(f"w_qkv: expected [{F}, {hidden}], got {list(w_qkv.shape)}")
+    for t, name in ((x, "x"), (w_qkv, "w_qkv"), (bias, "bias")):
+        if t is not None and t.dtype != pool.k_pages.dtype:
+            raise ValueError(f"{name}: dtype {t.dtype} differs from the pool's {pool.k_pages.dtype}")
+    if bias is not None and (not bias.is_contiguous() or tuple(bias.shape) != (F,)):
+        raise ValueError(f"bias must be a contiguous [{F}] tensor")
+    _positions(pos, n, rope)
+    qs = _head_rows(pool, q_out, "q_out", n) if q_out is not None else 0
+    dev = _pool_device(pool)
+    for t, name in ((x, "x"), (w_qkv, "w_qkv"), (bias, "bias"), (pos, "pos"), (q_out, "q_out")):
+        if t is not None:
+            _on_device(t, dev, name)
     r = None
     if rope is not None:
         (dt, dh, dw), theta = rope
         r = wf_rope(dt, dh, dw, float(theta))
-    qs = _row_stride(q_out, "q_out") if q_out is not None else 0
     rc = lib().wf_qkv_publish(ctypes.byref(pool.desc), ctypes.byref(r) if r else None, _ptr(x),
-                              x.stride(0), x.shape[1], _ptr(w_qkv), _ptr(bias), _ptr(pos),
-                              x.shape[0], dst_start, _ptr(q_out), qs, _stream(stream))
+                              x.stride(0), hidden, _ptr(w_qkv), _ptr(bias), _ptr(pos),
+                              n, dst_start, _ptr(q_out), qs, _stream(stream))
     _check(rc)
 
 
@@ -322,6 +432,7 @@ def wf_history_rotate(pool: KVPool, window_start: int, chunk_stride: int, n_chun
     table entries of the window [window_start, window_start + n_chunks *
     chunk_stride) rotate left by one chunk, in place; no page moves."""
     t = pool.page_table
+    _pool_device(pool)
     rc = lib().wf_history_rotate(_ptr(t), t.numel(), pool.page_size, window_start,
                                  chunk_stride, n_chunks, _stream(stream))
     _check(rc)

@@ -153,13 +153,96 @@ def test_device_status_null_arg(L):
 
 
 def test_binding_raises_with_message(L):
-    p = wf.KVPool.__new__(wf.KVPool)
-    p.desc = pool(page_size=100)
-    import torch
-    t = torch.empty(0)
+    rc, _ = attn(L, p=pool(page_size=100))
     with pytest.raises(wf.WFError, match="page_size"):
-        wf.wf_chunk_attn(p, [(0, 10, 0)], torch.empty(4, 4, 128), [0, 4], out=torch.empty(4, 4, 128),
-                         stream=0)
+        wf._check(rc)
+
+
+# ---- the binding's own checks (before any library call) --------------------
+# The C side sees raw pointers and checks strides, alignment and NULLs; the
+# binding checks what only the tensors know: device, element type and rows.
+# Every case here must raise ValueError without calling into the library.
+
+@pytest.fixture
+def no_lib(monkeypatch):
+    def forbidden():
+        raise AssertionError("the binding called the library before its own checks")
+    monkeypatch.setattr(wf, "lib", forbidden)
+
+
+def cpu_pool(heads=2, ps=16, D=128, pages=4, dtype=None):
+    import torch
+    dtype = dtype or torch.bfloat16
+    return wf.KVPool(torch.zeros(pages, heads, ps, D, dtype=dtype),
+                     torch.zeros(pages, heads, D, ps, dtype=dtype),
+                     torch.arange(pages, dtype=torch.int32))
+
+
+def test_binding_checks_attention_args(no_lib):
+    import torch
+    P = cpu_pool()
+    bf = torch.bfloat16
+    q = torch.zeros(40, 2, 128, dtype=bf)
+    segs, qss = [(0, 20, -1), (20, 20, 0), (40, 20, 1)], [0, 20, 40]
+    cases = [
+        (dict(q=torch.zeros(40, 3, 128, dtype=bf)), "q: expected"),
+        (dict(q=torch.zeros(39, 2, 128, dtype=bf)), "rows"),
+        (dict(q=q.float()), "dtype"),
+        (dict(out=torch.zeros(40, 2, 128)), "out: dtype"),
+        (dict(out=torch.zeros(30, 2, 128, dtype=bf)), "out: 30 rows"),
+        (dict(lse=torch.zeros(2, 40, dtype=torch.float64)), "lse"),
+        (dict(lse=torch.zeros(2, 39)), "lse: expected"),
+        (dict(lse=torch.zeros(3, 40)), "lse: expected"),
+        (dict(), "GPU tensor"),          # shapes fine: the pool lives on the host
+    ]
+    for kw, msg in cases:
+        args = dict(q=q, out=None, lse=None)
+        args.update(kw)
+        with pytest.raises(ValueError, match=msg):
+            wf.wf_chunk_attn(P, segs, args["q"], qss, out=args["out"], lse=args["lse"])
+    with pytest.raises(ValueError, match="lse"):
+        wf.wf_group_attn(P, [(0, 40)], [(0, 40, 0, 1)], q, lse=torch.zeros(2, 30))
+    with pytest.raises(ValueError, match="rows"):
+        wf.wf_group_attn(P, [(0, 40)], [(0, 41, 0, 1)], q)
+
+
+def test_binding_checks_publish_args(no_lib):
+    import torch
+    P = cpu_pool()
+    bf = torch.bfloat16
+    k = torch.zeros(10, 2, 128, dtype=bf)
+    pos = torch.zeros(10, 3, dtype=torch.int32)
+    rope = ((44, 42, 42), 1e4)
+    cases = [
+        (dict(v=torch.zeros(9, 2, 128, dtype=bf)), "v: 9 rows"),
+        (dict(v=torch.zeros(10, 2, 64, dtype=bf)), "v: expected"),
+        (dict(pos=torch.zeros(10, 3, dtype=torch.int64)), "pos"),
+        (dict(pos=torch.zeros(9, 3, dtype=torch.int32)), "pos"),
+        (dict(pos=None), "pos: required"),
+        (dict(q=torch.zeros(10, 2, 128)), "q: dtype"),
+        (dict(), "GPU tensor"),
+    ]
+    for kw, msg in cases:
+        args = dict(v=k, pos=pos, q=None)
+        args.update(kw)
+        with pytest.raises(ValueError, match=msg):
+            wf.wf_kv_publish(P, k, args["v"], 0, pos=args["pos"], rope=rope, q=args["q"])
+    x = torch.zeros(10, 256, dtype=bf)
+    w = torch.zeros(3 * 2 * 128, 256, dtype=bf)
+    for kw, msg in [(dict(w=torch.zeros(700, 256, dtype=bf)), "w_qkv"),
+                    (dict(bias=torch.zeros(10, dtype=bf)), "bias"),
+                    (dict(w=w.float()), "w_qkv: dtype"),
+                    (dict(), "GPU tensor")]:
+        a = dict(w=w, bias=None)
+        a.update(kw)
+        with pytest.raises(ValueError, match=msg):
+            wf.wf_qkv_publish(P, x, a["w"], 0, pos=pos, rope=rope, bias=a["bias"])
+    keys = wf.MXKeys(torch.zeros(4, 2, 8, 128, dtype=torch.uint8),
+                     torch.zeros(4, 2, 8, 4, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="MX keys"):
+        wf.wf_kv_publish_mx(P, keys, k, k, 0, pos=pos, rope=rope)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        wf.wf_history_rotate(P, 0, 16, 2)
 
 
 def gattn(L, p=None, runs=((0, 100), (100, 50), (150, 50)),
