@@ -9,6 +9,7 @@ in HBM before the timed region; the resident prefix (anchor + history) is
 published once before timing.
 
     python bench.py [--steps K] [--warmup W] [--config 4] [--no-cpu-baseline]
+                    [--no-long-tick]
 
 Prints one JSON line.  `value` is the unmasked attention TFLOP/s of the
 whole step (publish included in the time); `roofline` describes the
@@ -42,6 +43,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=4, choices=[2, 3, 4, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-long-tick", action="store_true",
+                    help="skip the long-context layer tick reported beside the headline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -108,50 +111,96 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
+_ORACLE = {}    # the sample's oracle inputs, set before the worker pool forks
+
+
+def _oracle_worker_init():
+    """One BLAS thread per worker: the pool supplies the parallelism."""
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
+    except Exception:
+        pass
+
+
+def _oracle_item(item):
+    """Attention of one (head, slot, row block) of the sample with the CPU
+    oracle as it stands; returns the item and its unmasked flops."""
+    from oracle.attention import chunk_attention
+    h, g, r0, r1, flops = item
+    d = _ORACLE
+    chunk_attention(d["k"], d["v"], d["table"], d["ps"], d["segs"], d["q"][r0:r1], [0, r1 - r0],
+                    d["first"] + g, d["scale"], d["dtype"], heads=[h])
+    return flops
+
+
+def cpu_cores() -> tuple:
+    """(workers, affinity): the CPUs this process may run on, capped by the
+    thread share the environment declares (OMP_NUM_THREADS), if any."""
+    aff = len(os.sched_getaffinity(0))
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    cap = int(env) if env.isdigit() and int(env) > 0 else aff
+    return max(1, min(aff, cap)), aff
+
+
 def cpu_baseline(cfg, seconds: float):
     """Time the CPU oracle (as it stands) on a bounded sample of the same
-    workload: whole heads of attention (all slots, all rows) until `seconds`
-    have passed, and a publish of 2048 tokens; scale both to a full step."""
-    import torch
-    from chunk_wise_causal_amd.workloads import make_workload
+    workload, on the host's cores: a process pool (one BLAS thread per
+    worker) over (head, slot, 1024-row block) items of a copy of the
+    configuration with at most 8 heads, head by head, until `seconds` have
+    passed; plus the oracle publish of the copy.  Both are scaled to one full
+    step.  Runs before the process touches the GPU (the pool forks)."""
     import dataclasses
-    from oracle.attention import chunk_attention
-    from oracle.publish import publish
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        threads = 1
-    # a copy of the configuration with at most 8 heads: same layout and pages
+    import multiprocessing
+    from chunk_wise_causal_amd.workloads import make_workload
+    from tests._pipeline import oracle_layer  # test glue: oracle-only pipeline
+    workers, aff = cpu_cores()
     small = dataclasses.replace(cfg, heads=min(cfg.heads, 8))
     wl = make_workload(small)
-    from tests._pipeline import oracle_layer  # test glue: oracle-only pipeline
     t0 = time.perf_counter()
     ref = oracle_layer(wl)
     t_pub_all = time.perf_counter() - t0
     c = wl.cfg
-    done_heads, t_attn = 0, 0.0
-    while done_heads < c.heads and t_attn < seconds:
+    qss = c.q_slot_start()
+    vis = [c.visible(g) for g in range(c.slots)]
+    items = [(h, g, r0, min(qss[g + 1], r0 + 1024),
+              4 * c.head_dim * (min(qss[g + 1], r0 + 1024) - r0) * vis[g])
+             for h in range(c.heads) for g in range(c.slots) for r0 in range(qss[g], qss[g + 1], 1024)]
+    _ORACLE.update(k=ref["k_pool"], v=ref["v_pool"], table=wl.page_table, ps=c.page_size,
+                   segs=c.segments(), q=ref["q"], first=0, scale=c.scale, dtype=c.dtype)
+    done_flops, done_items = 0, 0
+    ctx = multiprocessing.get_context("fork")
+    with ctx.Pool(workers, initializer=_oracle_worker_init) as pool:
         t0 = time.perf_counter()
-        chunk_attention(ref["k_pool"], ref["v_pool"], wl.page_table, c.page_size, c.segments(),
-                        ref["q"], c.q_slot_start(), 0, c.scale, c.dtype, heads=[done_heads])
-        t_attn += time.perf_counter() - t0
-        done_heads += 1
-    flops_per_head = cfg.unmasked_flops() / cfg.heads
-    attn_full = t_attn / done_heads * cfg.heads
+        pending, nxt = [], 0
+        while nxt < len(items) or pending:
+            # keep every worker busy until the budget is spent, then drain
+            while nxt < len(items) and len(pending) < 2 * workers and \
+                    time.perf_counter() - t0 < seconds:
+                pending.append(pool.apply_async(_oracle_item, (items[nxt],)))
+                nxt += 1
+            if not pending:
+                break
+            done_flops += pending.pop(0).get()
+            done_items += 1
+        t_attn = time.perf_counter() - t0
+    rate = done_flops / t_attn                           # unmasked flop/s of the oracle
+    attn_full = cfg.unmasked_flops() / rate
     # publish: the oracle published all n_kv tokens of the copy's heads
     pub_full = t_pub_all * (cfg.tick_tokens / c.n_kv) * (cfg.heads / c.heads)
     step = attn_full + pub_full
     return {
         "value": cfg.unmasked_flops() / step / 1e12,
         "unit": "TFLOP/s",
-        "cores": int(threads),
+        "cores": int(workers),
         "kind": "oracle",
-        "sample": (f"float64 numpy oracle: attention of {done_heads} head(s) x all "
-                   f"{cfg.slots} slots x {cfg.chunk} rows ({done_heads * flops_per_head:.3e} "
-                   f"unmasked flops, {t_attn:.1f} s) and publish of {c.n_kv} tokens x "
-                   f"{c.heads} heads ({t_pub_all:.1f} s), scaled by flops and bytes to one "
-                   f"full step ({step:.0f} s)"),
+        "sample": (f"float64 numpy oracle on {workers} worker processes (one BLAS thread each; "
+                   f"{aff} CPUs in the affinity set): attention of {done_items} (head, slot, "
+                   f"1024-row block) items of a {c.heads}-head copy of the workload "
+                   f"({done_flops:.3e} unmasked flops in {t_attn:.1f} s), publish of {c.n_kv} "
+                   f"tokens x {c.heads} heads ({t_pub_all:.1f} s, one process), scaled by flops "
+                   f"and bytes to one full step ({step:.0f} s)"),
+        "affinity_cpus": int(aff),
         "step_s_extrapolated": step,
     }
 
@@ -250,6 +299,76 @@ def time_qkv_publish(cfg, torch, wf, pos, steps: int):
             "unfused": "torch linear (library GEMM) + wf_kv_publish"}
 
 
+def time_publish_flushed(cfg, torch, wf, pool, k_t, v_t, pos_t, steps: int):
+    """The round's publish alone with the caches flushed before every launch
+    (a 512 MB device buffer is overwritten, more than the 4 MB L2 of each XCD
+    and the 256 MB MALL), so its reads and writes go to HBM: HIP events on
+    the launch stream around the publish only."""
+    stream = torch.cuda.current_stream()
+    rope = (cfg.rope, cfg.theta)
+    flush = torch.empty(256 << 20, dtype=torch.bfloat16, device="cuda")
+    ms = []
+    for i in range(steps + 2):
+        flush.fill_(float(i))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        wf.wf_kv_publish(pool, k_t, v_t, cfg.store_start, pos=pos_t, rope=rope, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if i >= 2:
+            ms.append(e0.elapsed_time(e1))
+    del flush
+    med = float(np.median(ms))
+    gbps = cfg.publish_bytes() / (med * 1e-3) / 1e9
+    return {"ms_p50": round(med, 4), "GBps": round(gbps, 1),
+            "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4),
+            "flush": "512 MB device buffer overwritten before each launch"}
+
+
+def time_layer_tick(cfg, torch, wf, steps: int, warmup: int):
+    """One layer tick of another configuration, timed like the headline:
+    the round's publish then the attention on one stream, HIP events around
+    each, inputs resident in HBM.  Its buffers are freed afterwards."""
+    q, k, v, pos, pool = device_inputs(cfg, torch, wf)
+    out = torch.empty_like(q)
+    ss, rope = cfg.store_start, (cfg.rope, cfg.theta)
+    wf.wf_kv_publish(pool, k[:ss], v[:ss], 0, pos=pos[:ss], rope=rope)
+    stream = torch.cuda.current_stream()
+    segs, qss = cfg.segments(), cfg.q_slot_start()
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        wf.wf_kv_publish(pool, k[ss:], v[ss:], ss, pos=pos[ss:], rope=rope, stream=stream)
+        if ev:
+            ev[1].record(stream)
+        wf.wf_chunk_attn(pool, segs, q, qss, 0, cfg.scale, out=out, stream=stream)
+        if ev:
+            ev[2].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    assert wf.wf_device_status() == 0
+    pub = float(np.median([e[0].elapsed_time(e[1]) for e in evs]))
+    att = float(np.median([e[1].elapsed_time(e[2]) for e in evs]))
+    tick = float(np.median([e[0].elapsed_time(e[2]) for e in evs]))
+    tf = cfg.unmasked_flops() / (att * 1e-3) / 1e12
+    gbps = cfg.publish_bytes() / (pub * 1e-3) / 1e9
+    del q, k, v, pos, pool, out
+    torch.cuda.empty_cache()
+    return {"workload": f"layer tick: {cfg.name}", "n_q": cfg.n_q, "n_kv": cfg.n_kv,
+            "unmasked_flops": cfg.unmasked_flops(), "steps": steps,
+            "tick_ms_p50": round(tick, 4), "attn_ms_p50": round(att, 4),
+            "attn_tflops": round(tf, 2), "attn_frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+            "publish_ms_p50": round(pub, 4), "publish_GBps": round(gbps, 1),
+            "publish_frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4)}
+
+
 def time_history_rotate(cfg, torch, wf, reps: int = 200):
     """End-of-round history rotation (wf_history_rotate) on the page-aligned
     placement of the same context: average launch duration over `reps`
@@ -289,10 +408,12 @@ def main():
     if args.copy_calibration:
         copy_calibration(torch)
         return
-    from chunk_wise_causal_amd import wf
     from chunk_wise_causal_amd.workloads import CONFIGS
-    wf.lib()
     cfg = CONFIGS[args.config]
+    # the oracle's worker pool forks: run it before the process touches the GPU
+    cpu = None if args.no_cpu_baseline else cpu_baseline(cfg, args.cpu_seconds)
+    from chunk_wise_causal_amd import wf
+    wf.lib()
     q, k, v, pos, pool = device_inputs(cfg, torch, wf)
     out = torch.empty_like(q)
     segs = cfg.segments()
@@ -368,11 +489,19 @@ def main():
                      "kernel": "attn_fwd_bf16<128, true>"},
         "cpu_baseline": None,
     }
+    res["publish_flushed"] = time_publish_flushed(cfg, torch, wf, pool, k_t, v_t, pos_t,
+                                                  args.steps)
     res["history_rotate"] = time_history_rotate(cfg, torch, wf)
     res["mx_variant"] = time_mx_variant(cfg, torch, wf, q, k, v, pos, pool, out, args.steps)
     res["qkv_publish"] = time_qkv_publish(cfg, torch, wf, pos, args.steps)
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
+    if args.config == 4 and not args.no_long_tick:
+        # the long-context layer tick (14B-like, chunk 10800, W=5) beside the
+        # headline: fewer steps, each about 85 ms
+        del q, k, v, pos, pool, out, k_t, v_t, pos_t
+        torch.cuda.empty_cache()
+        res["long_context_tick"] = time_layer_tick(CONFIGS[5], torch, wf,
+                                                   steps=max(3, args.steps // 2), warmup=2)
+    res["cpu_baseline"] = cpu
     print(json.dumps(res), flush=True)
 
 
