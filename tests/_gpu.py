@@ -103,3 +103,21 @@ LSE_ATOL_FP32 = 1e-5
 
 def lse_atol(dtype: str) -> float:
     return LSE_ATOL_BF16 if dtype == "bf16" else LSE_ATOL_FP32
+
+
+def record(kind: str, **fields) -> None:
+    """Append one parity figure to a JSON-lines file that outlives the test
+    run (pytest -q prints nothing of it): $WF_PARITY_RECORD, else
+    gpurun_out/parity_records.jsonl at the repository root."""
+    import json
+    import os
+    import time
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    path = os.environ.get("WF_PARITY_RECORD",
+                          os.path.join(root, "gpurun_out", "parity_records.jsonl"))
+    try:
+        os.makedirs(os.path.dirname(path), exist_ok=True)
+        with open(path, "a") as f:
+            f.write(json.dumps(dict(kind=kind, time=time.time(), **fields)) + "\n")
+    except OSError:
+        pass

@@ -2,7 +2,8 @@
 
 publish: bit-exact, byte for byte over the whole pool (written rows, NaN
 fill, stale pages).  attention: max-abs <= 2e-2 and relative RMS <= 5e-3
-against the float64 oracle; LSE within the derived bound (2.5e-3 bf16).  Shapes span several query and
+against the float64 oracle; LSE within the derived bound (4e-3 bf16, 1e-5
+fp32).  Shapes span several query and
 key tiles, ragged query tails, unaligned slot boundaries, every page-size
 regime (smaller than, equal to and larger than a 64-key tile), head_dim 64
 and 128, bf16 and fp32.
@@ -75,7 +76,11 @@ def test_attention_matches_oracle(case):
     got = G.to_f64(out)
     assert np.isfinite(got).all()
     mx, rr = G.err_stats(got, o_ref)
-    print(f"max-abs {mx:.3e} rel-rms {rr:.3e}", flush=True)
+    lse_err = float(np.abs(G.to_f64(lse) - l_ref).max())
+    print(f"max-abs {mx:.3e} rel-rms {rr:.3e} lse {lse_err:.2e}", flush=True)
+    G.record("attention", workload=c.name, dtype=c.dtype, heads=c.heads, head_dim=c.head_dim,
+             page_size=c.page_size, rows=c.n_q, keys=c.n_kv, max_abs=mx, rel_rms=rr,
+             lse_max=lse_err, all_elements=True)
     assert mx <= G.MAX_ABS and rr <= G.REL_RMS
     np.testing.assert_allclose(G.to_f64(lse), l_ref, rtol=0, atol=G.lse_atol(c.dtype))
     assert wf.wf_device_status() == 0
