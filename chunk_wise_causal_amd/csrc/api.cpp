@@ -577,11 +577,19 @@ int wf_qkv_publish(const wf_kv_pool* pool, const wf_rope* rope, const void* x,
   p.heads = pool->num_heads;
   p.ps_log2 = log2_exact(pool->page_size);
   p.num_pages = pool->num_pages;
-  p.tok_tiles = (n_tok + 255) / 256;
+  p.tok_tiles = (n_tok + wf::kQkvBlockTok - 1) / wf::kQkvBlockTok;
   p.sec0 = q_out ? 0 : 1;
-  p.feat_tiles = (3 - p.sec0) * pool->num_heads;
+  // blocks of two heads over the computed heads (2H without Q, 3H with)
+  p.feat_tiles = ((3 - p.sec0) * pool->num_heads + 1) / 2;
   p.rope = rope ? 1 : 0;
-  if (rope) fill_pairs(rope, p.pair_axis, p.pair_omega);
+  if (rope) {
+    int32_t axis[wf::kMaxPairs];
+    fill_pairs(rope, axis, p.pair_omega);
+    p.band0[0] = 0;
+    p.band0[1] = rope->d_t / 2;
+    p.band0[2] = (rope->d_t + rope->d_h) / 2;
+    p.band0[3] = pool->head_dim / 2;
+  }
   if ((int64_t)p.feat_tiles * p.tok_tiles > 0x7fffffff)
     return fail(WF_ERR_UNSUPPORTED, "projection too large");
   hipError_t e;

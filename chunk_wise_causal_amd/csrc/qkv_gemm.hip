@@ -13,67 +13,69 @@
 // a run of 4 consecutive features in 4 consecutive accumulator registers, so
 // a RoPE pair (2i, 2i+1) is two registers of one lane.
 //
-// Block: 128 features (one head of one of Q, K, V) x 256 tokens, 8 waves of
-// 64 features x 64 tokens (four 32x32 accumulators each; two waves per
-// SIMD, so one wave's epilogue or wait overlaps the other's products).
-// k-tiles of 64 go straight from global memory into a three-slot LDS ring
-// (global_load_lds_dwordx4, two tiles ahead), 16-byte chunks XOR-swizzled by
-// row so that the fragment reads of 8 consecutive rows hit distinct banks;
-// one barrier per k-tile.  Blocks are dealt to the XCDs in contiguous runs,
-// and a run walks 2 token tiles per feature tile, so the blocks resident on
-// one XCD share weight and hidden-state tiles in its L2.
+// Block: 256 features (two heads) x 256 tokens, 8 waves of 128 features (one
+// head) x 64 tokens, eight 32x32 accumulators per wave (two waves per SIMD).
+// Per k-step of 16 a wave reads 6 fragments for 8 products.  k-tiles of 32
+// go straight from global memory into a four-slot LDS ring
+// (global_load_lds_dwordx4, three tiles in flight, 32 KB per tile), 16-byte
+// chunks of the 64-byte rows XOR-swizzled so that the fragment reads of 16
+// consecutive rows hit distinct banks; one barrier per k-tile.  Per CU and
+// clock the block needs 32 bytes of L2 traffic at the full matrix rate, half
+// of what a 128 x 256 block needs, against the ~64 B/clk an MI355X CU fills
+// from its L2.  Blocks are dealt to the XCDs in contiguous runs of 4 feature
+// x 8 token tiles (qkv_tile in wf_qkv.h).
+//
+// Rotary factors: for the video layout a block's 256 tokens take few
+// distinct positions per axis, so the block evaluates the factors once per
+// (pair, position) present - the per-axis position ranges of its tokens -
+// into an LDS table while its first tiles load; the epilogue then looks them
+// up.  Positions spread too widely for the table fall back to evaluating the
+// factors per element (same values, more time).
 //
 // Epilogue per element: + bias, round to bf16 (the unfused projection's
 // output), then for Q and K the rotation of wf_kv_publish (double-precision
 // angle and cos/sin rounded to float, float products and sums without fused
-// multiply-add, round to bf16), then Q to q_out, K to its page row, V to its
-// d-major page column.
+// multiply-add, round to bf16).  The results are staged in the ring's LDS,
+// one wave's 64 tokens of one head at a time, and re-read in the output's own
+// order, so that every global store is 16 bytes: Q rows, K page rows (256
+// contiguous bytes per token) and V page columns (8 consecutive tokens of a
+// feature, d-major).
 #include "../../include/wf.h"
+#include "wf_numerics.h"
 #include "wf_qkv.h"
 
 namespace wf {
 namespace {
 
-constexpr int TM = 128;    // features per block (one head)
-constexpr int TN = 256;    // tokens per block
-constexpr int TK = 64;     // hidden elements per k-tile
-constexpr int NTH = 512;   // threads per block (8 waves)
-constexpr int NSL = 3;     // LDS ring slots
-constexpr int GT = 2;      // token tiles per feature tile in the block order
-constexpr int A_BYTES = TM * TK * 2;           // 16 KB
-constexpr int B_BYTES = TN * TK * 2;           // 32 KB
-constexpr int SLOT_BYTES = A_BYTES + B_BYTES;  // 48 KB
-constexpr int A_DMA = A_BYTES / (NTH * 16);    // 16-byte loads per thread per k-tile: 2
-constexpr int B_DMA = B_BYTES / (NTH * 16);    // 4
+constexpr int BM = kQkvBlockFeat;          // 256 features per block
+constexpr int BN = kQkvBlockTok;           // 256 tokens per block
+constexpr int D = 128;                     // head_dim
+constexpr int TK = 32;                     // hidden elements per k-tile
+constexpr int NTH = 512;                   // 8 waves: 2 heads x 4 token quarters
+constexpr int NSL = 4;                     // LDS ring slots
+constexpr int ROWB = TK * 2;               // bytes per tile row: 64
+constexpr int A_BYTES = BM * ROWB;         // 16 KB of W rows per tile
+constexpr int B_BYTES = BN * ROWB;         // 16 KB of x rows per tile
+constexpr int SLOT = A_BYTES + B_BYTES;    // 32 KB
+constexpr int RING = NSL * SLOT;           // 128 KB
+constexpr int A_DMA = A_BYTES / (NTH * 16);  // 16-byte loads per thread per tile: 2
+constexpr int B_DMA = B_BYTES / (NTH * 16);  // 2
 constexpr int DMAS = A_DMA + B_DMA;
+constexpr int NPAIR = D / 2;
+// past the ring: the positions of the block's tokens (int4 per token), the
+// per-wave position minima/maxima, the per-pair table row bases, then the
+// (cos, sin) table; the whole LDS is 160 KB
+constexpr int POS_OFF = RING;                  // int4[BN]
+constexpr int HDR_OFF = POS_OFF + BN * 16;     // int[32]: 4 waves x (3 minima, 3 maxima)
+constexpr int RB_OFF = HDR_OFF + 32 * 4;       // int[NPAIR]
+constexpr int TAB_OFF = RB_OFF + NPAIR * 4;
+constexpr int LDS_BYTES = 160 * 1024;
+constexpr int TAB_CAP = (LDS_BYTES - TAB_OFF) / 8;
+static_assert(A_DMA == 2 && B_DMA == 2, "two loads of each operand per thread and tile");
+static_assert(2 * 64 * D * 2 <= RING && 2 * D * BN * 2 <= RING, "staging fits in the ring");
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
-
-__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
-
-// byte offset of logical 16-byte chunk c (0..7) of row r in an LDS tile of
-// 128-byte rows
-__device__ __forceinline__ int tile_off(int r, int c) { return r * 128 + ((c ^ (r & 7)) << 4); }
-
-// y0 = x0*c - x1*s, y1 = x0*s + x1*c, every operation rounded on its own
-__device__ __forceinline__ void rotate(float x0, float x1, float cs, float sn, float& y0,
-                                       float& y1) {
-#pragma clang fp contract(off)
-  const float a = x0 * cs;
-  const float b = x1 * sn;
-  const float c = x0 * sn;
-  const float d = x1 * cs;
-  y0 = a - b;
-  y1 = c + d;
-}
 
 // Direct global->LDS load, 16 bytes per lane: lane i writes LDS bytes
 // [M0 + 16 i, +16) with M0 = lds + OFF (inline assembly, so that the
@@ -92,197 +94,445 @@ __device__ __forceinline__ void dma16(const char* sbase, uint32_t voff, uint32_t
       : "memory", "m0", "scc");
 }
 
-// chunks I.. of one operand: chunk i goes 8 KB (one instruction of all 8
-// waves, 64 rows) further than chunk i-1
-template <uint32_t OFF, int I, int N>
-__device__ __forceinline__ void dma_rows(const char* base, const uint32_t* off, uint32_t lds) {
-  if constexpr (I < N) {
-    dma16<OFF + I * 8192>(base, off[I], lds);
-    dma_rows<OFF, I + 1, N>(base, off, lds);
-  }
+// Fragments of one k-tile for a wave: A = W rows 128 wm + 32 i + ql (i < 4),
+// B = x rows 64 wn + 32 j + ql (j < 2), for the two k-steps; `ra` and `rb`
+// are the lane's row bases in the slot, xo[ks] its swizzled chunk offset.
+struct Frags {
+  bf16x8 a[2][4], b[2][2];
+};
+
+// one fragment read of the 12 of a tile (n < 12): k-step n / 6, then
+// A 0..3, B 0..1
+template <int N>
+__device__ __forceinline__ void read_frag(Frags& f, const char* slot, int ra, int rb,
+                                          const int* xo) {
+  constexpr int ks = N / 6, r = N % 6;
+  if constexpr (r < 4)
+    f.a[ks][r] = *reinterpret_cast<const bf16x8*>(slot + ra + xo[ks] + r * 32 * ROWB);
+  else
+    f.b[ks][r - 4] = *reinterpret_cast<const bf16x8*>(slot + rb + xo[ks] + (r - 4) * 32 * ROWB);
 }
 
-// the k-tile at hidden offset k0 into ring slot SLOT: A_DMA chunks of W rows,
-// B_DMA of x rows per thread; each wave instruction fills 1 KB (8 rows)
-template <int SLOT>
-__device__ __forceinline__ void load_tile(const char* wbase, const char* xbase, int k0,
-                                          const uint32_t* aoff, const uint32_t* boff,
-                                          uint32_t wave_lds) {
-  static_assert(NTH * 16 == 8192, "one instruction of every wave fills 8 KB");
-  dma_rows<SLOT * SLOT_BYTES, 0, A_DMA>(wbase + 2 * k0, aoff, wave_lds);
-  dma_rows<SLOT * SLOT_BYTES + A_BYTES, 0, B_DMA>(xbase + 2 * k0, boff, wave_lds);
+// product n of the 16 of a tile: k-step n / 8, accumulator (i, j) = n % 8
+template <int N>
+__device__ __forceinline__ void mma(const Frags& f, f32x16 (&acc)[4][2]) {
+  constexpr int ks = N / 8, i = (N % 8) / 2, j = N % 2;
+  acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[ks][i], f.b[ks][j], acc[i][j], 0, 0, 0);
 }
 
-__device__ __forceinline__ void load_slot(int slot, const char* wbase, const char* xbase, int k0,
-                                          const uint32_t* aoff, const uint32_t* boff,
-                                          uint32_t wave_lds) {
-  if (slot == 0) load_tile<0>(wbase, xbase, k0, aoff, boff, wave_lds);
-  else if (slot == 1) load_tile<1>(wbase, xbase, k0, aoff, boff, wave_lds);
-  else load_tile<2>(wbase, xbase, k0, aoff, boff, wave_lds);
+// the scheduler keeps the source order across this point
+__device__ __forceinline__ void fence() { __builtin_amdgcn_sched_barrier(0); }
+
+__device__ __forceinline__ int wave_min(int v) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) v = min(v, __shfl_xor(v, m));
+  return v;
 }
 
-// fragments of k-step ks: A rows 64wm + 32i + ql, B rows 64wn + 32j + ql
-__device__ __forceinline__ void frags(const char* slot_base, int ks, int wm, int wn, int ql,
-                                      int hg, bf16x8* a, bf16x8* bv) {
-  const int c = 2 * ks + hg;
+__device__ __forceinline__ int wave_max(int v) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-    a[i] = *reinterpret_cast<const bf16x8*>(slot_base + tile_off(64 * wm + 32 * i + ql, c));
-#pragma unroll
-  for (int j = 0; j < 2; ++j)
-    bv[j] = *reinterpret_cast<const bf16x8*>(slot_base + A_BYTES +
-                                              tile_off(64 * wn + 32 * j + ql, c));
+  for (int m = 1; m < 64; m <<= 1) v = max(v, __shfl_xor(v, m));
+  return v;
 }
 
-// The 4 accumulators of a wave += one k-tile of its slot.  The fragments of
-// k-step ks+1 are read while the 4 products of k-step ks run.
-__device__ __forceinline__ void mma_tile(const char* slot_base, int wm, int wn, int ql, int hg,
-                                         f32x16 (&acc)[2][2]) {
-  bf16x8 a[2][2], bv[2][2];
-  frags(slot_base, 0, wm, wn, ql, hg, a[0], bv[0]);
-#pragma unroll
-  for (int ks = 0; ks < TK / 16; ++ks) {
-    const int cur = ks & 1;
-    if (ks + 1 < TK / 16) frags(slot_base, ks + 1, wm, wn, ql, hg, a[cur ^ 1], bv[cur ^ 1]);
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cur][i], bv[cur][j], acc[i][j],
-                                                            0, 0, 0);
-    if (ks + 1 < TK / 16) {
-      // reads of the next k-step spread over this k-step's products
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-    }
-  }
+__device__ __forceinline__ int axis_of(const QkvParams& p, int pr) {
+  return (pr >= p.band0[1]) + (pr >= p.band0[2]);
+}
+
+// Loads of tile m into ring slot m % 4 (M0 base `dst` = this wave's 1 KB
+// of the slot).  Tiles past the last one re-load the last tile into a slot
+// no step reads again, so every step issues the same loads and the wait
+// counts are constants.
+__device__ __forceinline__ void load_tile_at(const char* wbase, const char* xbase, int m,
+                                             int ktiles, const uint32_t* aoff,
+                                             const uint32_t* boff, uint32_t wave_lds) {
+  const int kb = min(m, ktiles - 1) * TK * 2;
+  const uint32_t dst = wave_lds + (uint32_t)(m % NSL) * SLOT;
+  dma16<0>(wbase + kb, aoff[0], dst);
+  dma16<8192>(wbase + kb, aoff[1], dst);
+  dma16<A_BYTES>(xbase + kb, boff[0], dst);
+  dma16<A_BYTES + 8192>(xbase + kb, boff[1], dst);
+}
+
+// the 16 products of the tile whose fragments are in `cur`
+__device__ __forceinline__ void mma_all(const Frags& cur, f32x16 (&acc)[4][2]) {
+  mma<0>(cur, acc); mma<1>(cur, acc); mma<2>(cur, acc); mma<3>(cur, acc);
+  mma<4>(cur, acc); mma<5>(cur, acc); mma<6>(cur, acc); mma<7>(cur, acc);
+  mma<8>(cur, acc); mma<9>(cur, acc); mma<10>(cur, acc); mma<11>(cur, acc);
+  mma<12>(cur, acc); mma<13>(cur, acc); mma<14>(cur, acc); mma<15>(cur, acc);
+}
+
+// Step kt < ktiles - 1 of the k-loop (B = kt % 2: fragment buffer B holds
+// tile kt, the other one receives tile kt+1).  Tile kt+1 is done for this
+// thread when only the loads of tiles kt+2 and kt+3 are in flight, and this
+// wave's reads of tile kt are done; after the barrier tile kt+1 is visible
+// and tile kt's slot is free for tile kt+4.
+template <int B>
+__device__ __forceinline__ void k_step(int kt, int ktiles, const char* lds, const char* wbase,
+                                       const char* xbase, const uint32_t* aoff,
+                                       const uint32_t* boff, uint32_t wave_lds, int ra, int rb,
+                                       const int* xo, Frags (&fr)[2], f32x16 (&acc)[4][2]) {
+  const Frags& cur = fr[B];
+  Frags& nxt = fr[B ^ 1];
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(2 * DMAS) : "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  const char* nslot = lds + ((kt + 1) % NSL) * SLOT;
+  const int kb = min(kt + NSL, ktiles - 1) * TK * 2;
+  const uint32_t dst = wave_lds + (uint32_t)(kt % NSL) * SLOT;
+  fence();
+  mma<0>(cur, acc);
+  fence();
+  dma16<0>(wbase + kb, aoff[0], dst);
+  fence();
+  mma<1>(cur, acc);
+  fence();
+  dma16<8192>(wbase + kb, aoff[1], dst);
+  fence();
+  mma<2>(cur, acc);
+  fence();
+  dma16<A_BYTES>(xbase + kb, boff[0], dst);
+  fence();
+  mma<3>(cur, acc);
+  fence();
+  dma16<A_BYTES + 8192>(xbase + kb, boff[1], dst);
+  fence();
+  mma<4>(cur, acc);
+  read_frag<0>(nxt, nslot, ra, rb, xo);
+  read_frag<1>(nxt, nslot, ra, rb, xo);
+  fence();
+  mma<5>(cur, acc);
+  read_frag<2>(nxt, nslot, ra, rb, xo);
+  read_frag<3>(nxt, nslot, ra, rb, xo);
+  fence();
+  mma<6>(cur, acc);
+  read_frag<4>(nxt, nslot, ra, rb, xo);
+  read_frag<5>(nxt, nslot, ra, rb, xo);
+  fence();
+  mma<7>(cur, acc);
+  read_frag<6>(nxt, nslot, ra, rb, xo);
+  read_frag<7>(nxt, nslot, ra, rb, xo);
+  fence();
+  mma<8>(cur, acc);
+  read_frag<8>(nxt, nslot, ra, rb, xo);
+  read_frag<9>(nxt, nslot, ra, rb, xo);
+  fence();
+  mma<9>(cur, acc);
+  read_frag<10>(nxt, nslot, ra, rb, xo);
+  read_frag<11>(nxt, nslot, ra, rb, xo);
+  fence();
+  mma<10>(cur, acc);
+  mma<11>(cur, acc);
+  mma<12>(cur, acc);
+  mma<13>(cur, acc);
+  mma<14>(cur, acc);
+  mma<15>(cur, acc);
 }
 
 __global__ __attribute__((amdgpu_flat_work_group_size(NTH, NTH)))
 void qkv_gemm_publish(const QkvParams p) {
-  __shared__ __attribute__((aligned(16))) char lds[NSL * SLOT_BYTES];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
+  int* hdr = reinterpret_cast<int*>(lds + HDR_OFF);
+  int* rbt = reinterpret_cast<int*>(lds + RB_OFF);
+  const int4* post = reinterpret_cast<const int4*>(lds + POS_OFF);
+  float2* tab = reinterpret_cast<float2*>(lds + TAB_OFF);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 1, wn = wave >> 1;
   const int ql = lane & 31, hg = lane >> 5;
 
-  // ---- block -> (feature tile, token tile) ----------------------------------
-  const int nb = gridDim.x, b = blockIdx.x;
-  const int per = nb >> 3;
-  const int w = (b < (per << 3)) ? ((b & 7) * per + (b >> 3)) : b;
-  // groups of GT token tiles; inside a group, feature tile major
-  const int group_tiles = GT * p.feat_tiles;
-  const int g = w / group_tiles, rem = w - g * group_tiles;
-  const int tiles_in_g = min(GT, p.tok_tiles - g * GT);
-  const int ftile = rem / tiles_in_g;
-  const int ttile = g * GT + (rem - ftile * tiles_in_g);
-  const int sec = p.sec0 + ftile / p.heads;            // 0 Q, 1 K, 2 V
-  const int head = ftile % p.heads;
-  const int f0 = (sec * p.heads + head) * TM;          // first W row
-  const int t0 = ttile * TN;
+  // ---- block -> (two heads, 256 tokens) --------------------------------------
+  const QkvTile tl = qkv_tile(blockIdx.x, gridDim.x, p.feat_tiles, p.tok_tiles);
+  const int t0 = tl.ttile * BN;
+  const int n_heads = (3 - p.sec0) * p.heads;     // heads computed: [K | V] or [Q | K | V]
+  const int gh0 = p.sec0 * p.heads + 2 * tl.ftile;  // global head of wm = 0 (section-major)
+  const int gh_last = 3 * p.heads - 1;
+  const int wrow0 = gh0 * D;                        // first W row of the block
 
-  // ---- load addressing: thread q fills LDS byte 8192 i + 16 q of a tile,
-  // i.e. row 64 i + q / 8, physical chunk q % 8 = logical chunk ^ (row & 7)
-  const char* wbase = reinterpret_cast<const char*>(p.w + (int64_t)f0 * p.hidden);
+  // ---- load addressing: instruction u of this thread fills LDS row
+  // r = 16 (8u + wave) + lane / 4, physical chunk lane % 4, which holds the
+  // logical chunk (lane % 4) ^ ((r >> 2) & 3) of row r.  Rows past the last
+  // head or token re-read the last one (their results are never stored), so
+  // no load leaves w or x.
+  const char* wbase = reinterpret_cast<const char*>(p.w + (int64_t)wrow0 * p.hidden);
   const char* xbase = reinterpret_cast<const char*>(p.x + (int64_t)t0 * p.x_stride);
   uint32_t aoff[A_DMA], boff[B_DMA];
-  {
-    const int r0 = tid >> 3, pc = tid & 7;
-    const int lc = pc ^ (r0 & 7);
 #pragma unroll
-    for (int i = 0; i < A_DMA; ++i)
-      aoff[i] = (uint32_t)(((64 * i + r0) * p.hidden + lc * 8) * 2);
-#pragma unroll
-    for (int i = 0; i < B_DMA; ++i) {
-      // rows past the last token re-read the last token (their results are
-      // never stored), so no load leaves x
-      const int r = min(64 * i + r0, p.n_tok - 1 - t0);
-      boff[i] = (uint32_t)((r * p.x_stride + lc * 8) * 2);
-    }
+  for (int u = 0; u < 2; ++u) {
+    const int r = 16 * (8 * u + wave) + (lane >> 2);
+    const int lc = (lane & 3) ^ ((r >> 2) & 3);
+    const int wr = min(wrow0 + r, (gh_last + 1) * D - 1) - wrow0;
+    const int xr = min(t0 + r, p.n_tok - 1) - t0;
+    aoff[u] = (uint32_t)(wr * p.hidden * 2 + lc * 16);
+    boff[u] = (uint32_t)(xr * (int)p.x_stride * 2 + lc * 16);
   }
-  const uint32_t wave_lds =
-      (uint32_t)(uintptr_t)lds + (uint32_t)__builtin_amdgcn_readfirstlane(wave) * 1024u;
-
-  f32x16 acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+  const uint32_t wave_lds = (uint32_t)(uintptr_t)lds + (uint32_t)wave * 1024u;
 
   const int ktiles = p.hidden / TK;
-  load_slot(0, wbase, xbase, 0, aoff, boff, wave_lds);
-  if (ktiles > 1) load_slot(1, wbase, xbase, TK, aoff, boff, wave_lds);
-  for (int kt = 0; kt < ktiles; ++kt) {
-    // this thread's loads of tile kt are done when at most the next tile's
-    // are still in flight; the barrier then publishes every thread's
-    if (kt + 1 < ktiles) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(DMAS) : "memory");
-    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    // slot (kt + 2) % 3 was last read in step kt - 1, which every wave has
-    // left (barrier above)
-    if (kt + 2 < ktiles) load_slot((kt + 2) % NSL, wbase, xbase, (kt + 2) * TK, aoff, boff, wave_lds);
-    mma_tile(lds + (kt % NSL) * SLOT_BYTES, wm, wn, ql, hg, acc);
+  // tiles 0 .. 2
+  load_tile_at(wbase, xbase, 0, ktiles, aoff, boff, wave_lds);
+  load_tile_at(wbase, xbase, 1, ktiles, aoff, boff, wave_lds);
+  load_tile_at(wbase, xbase, 2, ktiles, aoff, boff, wave_lds);
+
+  // ---- rotary factor table (while the first tiles load) ---------------------
+  // the block needs it if its first head is Q or K (heads are section-major)
+  const bool rot_block = p.rope && gh0 < 2 * p.heads;
+  bool use_tab = false;
+  int mn[3] = {0, 0, 0};
+  if (rot_block) {
+    if (tid < BN) {
+      // rows past the last token repeat it: min and max unchanged
+      const int64_t t = min(t0 + tid, p.n_tok - 1);
+      const int4 v = make_int4(p.pos[t * 3], p.pos[t * 3 + 1], p.pos[t * 3 + 2], 0);
+      reinterpret_cast<int4*>(lds + POS_OFF)[tid] = v;
+      const int lo0 = wave_min(v.x), lo1 = wave_min(v.y), lo2 = wave_min(v.z);
+      const int hi0 = wave_max(v.x), hi1 = wave_max(v.y), hi2 = wave_max(v.z);
+      if (lane == 0) {
+        hdr[wave * 6 + 0] = lo0;
+        hdr[wave * 6 + 1] = lo1;
+        hdr[wave * 6 + 2] = lo2;
+        hdr[wave * 6 + 3] = hi0;
+        hdr[wave * 6 + 4] = hi1;
+        hdr[wave * 6 + 5] = hi2;
+      }
+    }
+    __syncthreads();
+    int64_t rng[3], off[4];
+    off[0] = 0;
+#pragma unroll
+    for (int a = 0; a < 3; ++a) {
+      int lo = hdr[a], hi = hdr[3 + a];
+#pragma unroll
+      for (int w = 1; w < BN / 64; ++w) {
+        lo = min(lo, hdr[w * 6 + a]);
+        hi = max(hi, hdr[w * 6 + 3 + a]);
+      }
+      mn[a] = lo;
+      rng[a] = (int64_t)hi - lo + 1;
+      off[a + 1] = off[a] + (int64_t)(p.band0[a + 1] - p.band0[a]) * rng[a];
+    }
+    use_tab = off[3] <= TAB_CAP;
+    if (use_tab) {
+      // entry off[a] + (pr - band0[a]) * rng[a] + (pos - mn[a]) = rb[pr] + pos;
+      // the per-axis values are picked with selects (a runtime index into a
+      // small array would put it in scratch memory)
+      const int o1 = (int)off[1], o2 = (int)off[2], r0 = (int)rng[0], r1 = (int)rng[1],
+                r2 = (int)rng[2];
+      if (tid < NPAIR) {
+        const int a = axis_of(p, tid);
+        const int oa = a == 0 ? 0 : (a == 1 ? o1 : o2);
+        const int ra_ = a == 0 ? r0 : (a == 1 ? r1 : r2);
+        const int ma = a == 0 ? mn[0] : (a == 1 ? mn[1] : mn[2]);
+        const int b0 = a == 0 ? p.band0[0] : (a == 1 ? p.band0[1] : p.band0[2]);
+        rbt[tid] = oa + (tid - b0) * ra_ - ma;
+      }
+      for (int e = tid; e < (int)off[3]; e += NTH) {
+        const int a = (e >= o1) + (e >= o2);
+        const int oa = a == 0 ? 0 : (a == 1 ? o1 : o2);
+        const int ra_ = a == 0 ? r0 : (a == 1 ? r1 : r2);
+        const int ma = a == 0 ? mn[0] : (a == 1 ? mn[1] : mn[2]);
+        const int b0 = a == 0 ? p.band0[0] : (a == 1 ? p.band0[1] : p.band0[2]);
+        const int within = e - oa;
+        const int pr = b0 + within / ra_;
+        tab[e] = rotary_factors(ma + within % ra_, p.pair_omega[pr]);
+      }
+    }
+    // visible to every wave after the k-loop's barriers
   }
 
-  // ---- epilogue ------------------------------------------------------------
+  // ---- k-loop ----------------------------------------------------------------
+  // Software pipeline over k-tiles: step kt waits for tile kt+1, takes the
+  // barrier (every wave has read tile kt, so its slot is free; tile kt+1 is
+  // visible), then issues the products of tile kt from registers with the
+  // loads of tile kt+4 into tile kt's slot and the fragment reads of tile
+  // kt+1 placed between them, so the matrix pipe is fed across the barrier.
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+  const int sw = (ql >> 2) & 3;   // rows 32 i + ql: (row >> 2) & 3 depends on ql only
+  const int xo[2] = {(hg ^ sw) << 4, ((2 + hg) ^ sw) << 4};
+  const int ra = (128 * wm + ql) * ROWB;
+  const int rbo = A_BYTES + (64 * wn + ql) * ROWB;
+  Frags fr[2];
+
+  // tile 0: visible after this thread's loads of it are done and the barrier
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * DMAS) : "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  load_tile_at(wbase, xbase, NSL - 1, ktiles, aoff, boff, wave_lds);
+  read_frag<0>(fr[0], lds, ra, rbo, xo);
+  read_frag<1>(fr[0], lds, ra, rbo, xo);
+  read_frag<2>(fr[0], lds, ra, rbo, xo);
+  read_frag<3>(fr[0], lds, ra, rbo, xo);
+  read_frag<4>(fr[0], lds, ra, rbo, xo);
+  read_frag<5>(fr[0], lds, ra, rbo, xo);
+  read_frag<6>(fr[0], lds, ra, rbo, xo);
+  read_frag<7>(fr[0], lds, ra, rbo, xo);
+  read_frag<8>(fr[0], lds, ra, rbo, xo);
+  read_frag<9>(fr[0], lds, ra, rbo, xo);
+  read_frag<10>(fr[0], lds, ra, rbo, xo);
+  read_frag<11>(fr[0], lds, ra, rbo, xo);
+
+  // steps 0 .. ktiles-2 (tile m's fragments in buffer m % 2), then the
+  // products of the last tile; ktiles = hidden / 32 is even
+  for (int kt = 0; kt < ktiles - 2; kt += 2) {
+    k_step<0>(kt, ktiles, lds, wbase, xbase, aoff, boff, wave_lds, ra, rbo, xo, fr, acc);
+    k_step<1>(kt + 1, ktiles, lds, wbase, xbase, aoff, boff, wave_lds, ra, rbo, xo, fr, acc);
+  }
+  k_step<0>(ktiles - 2, ktiles, lds, wbase, xbase, aoff, boff, wave_lds, ra, rbo, xo, fr, acc);
+  mma_all(fr[1], acc);
+  // the loads of the re-loaded tiles past the last one land in slots no one
+  // reads; they complete before the staging area is written
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  // ---- epilogue ----------------------------------------------------------------
+  // Phase 1: every wave writes its 64 tokens of its head, + bias and rounded
+  // to bf16, into the stage (the ring's LDS).  Phase 2: the wave re-reads its
+  // own part in the output's order; Q and K are rotated there (the
+  // accumulators are dead by then), and every global store is 16 bytes.
+  __syncthreads();   // every wave is done with the ring: it becomes the stage
+  const int hs = 2 * tl.ftile + wm;   // this wave's head among the computed ones
+  if (hs >= n_heads) return;
+  const int gh = gh0 + wm;
+  const int sec = gh / p.heads, head = gh - sec * p.heads;
+  char* stage = lds + wm * (RING / 2);
   const int ps = 1 << p.ps_log2;
-  int bad = 0;
+  const bool bias8 = p.bias && (reinterpret_cast<uintptr_t>(p.bias) & 7) == 0;
+  // K and V: the page of the wave's token 64 wn + lane, read before phase 1
+  // so that its latency hides behind it; phase 2 takes a token's page from
+  // its lane (one dependent table read per token instead of per store)
+  int pg = 0;
+  if (sec >= 1) {
+    const int t = t0 + 64 * wn + lane;
+    if (t < p.n_tok) pg = p.page_table[(p.dst_start + t) >> p.ps_log2];
+  }
+
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int t = t0 + 64 * wn + 32 * j + ql;
-    if (t >= p.n_tok) continue;
-    int page = -1, prow = 0;
-    if (sec > 0) {
-      const int L = p.dst_start + t;
-      page = p.page_table[L >> p.ps_log2];
-      if ((unsigned)page >= (unsigned)p.num_pages) {
-        bad = 1;
-        continue;
-      }
-      prow = L & (ps - 1);
-    }
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        // features fl .. fl+3 of the head: registers 4q4 .. 4q4+3
-        const int fl = 64 * wm + 32 * i + 8 * q4 + 4 * hg;
-        uint16_t o[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float v = acc[i][j][4 * q4 + e];
-          if (p.bias) v += bf16_to_f32(p.bias[f0 + fl + e]);
-          o[e] = f32_to_bf16_rne(v);
-        }
-        if (sec < 2 && p.rope) {
-#pragma unroll
-          for (int e = 0; e < 4; e += 2) {
-            const int pr = (fl + e) >> 1;
-            const double phi = (double)p.pos[(int64_t)t * 3 + p.pair_axis[pr]] * p.pair_omega[pr];
-            double sn, cn;
-            sincos(phi, &sn, &cn);
-            float y0, y1;
-            rotate(bf16_to_f32(o[e]), bf16_to_f32(o[e + 1]), (float)cn, (float)sn, y0, y1);
-            o[e] = f32_to_bf16_rne(y0);
-            o[e + 1] = f32_to_bf16_rne(y1);
-          }
-        }
-        const uint2 packed = make_uint2((uint32_t)o[0] | ((uint32_t)o[1] << 16),
-                                        (uint32_t)o[2] | ((uint32_t)o[3] << 16));
-        if (sec == 0) {
-          *reinterpret_cast<uint2*>(p.q_out + (int64_t)t * p.q_stride + head * TM + fl) = packed;
-        } else if (sec == 1) {
-          *reinterpret_cast<uint2*>(
-              p.k_pages + (((int64_t)page * p.heads + head) * ps + prow) * TM + fl) = packed;
+    for (int q4 = 0; q4 < 4; ++q4) {
+      // features fl .. fl+3 of the head: registers 4 q4 .. 4 q4 + 3
+      const int fl = 32 * i + 8 * q4 + 4 * hg;
+      float bv[4] = {0.f, 0.f, 0.f, 0.f};
+      if (p.bias) {
+        const uint16_t* bp = p.bias + gh * D + fl;
+        if (bias8) {
+          const uint2 b2 = *reinterpret_cast<const uint2*>(bp);
+          bv[0] = __uint_as_float(b2.x << 16);
+          bv[1] = __uint_as_float(b2.x & 0xffff0000u);
+          bv[2] = __uint_as_float(b2.y << 16);
+          bv[3] = __uint_as_float(b2.y & 0xffff0000u);
         } else {
-          uint16_t* vcol = p.v_pages + (((int64_t)page * p.heads + head) * TM + fl) * ps + prow;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) vcol[(int64_t)e * ps] = o[e];
+          for (int e = 0; e < 4; ++e) bv[e] = bf16_to_f32(bp[e]);
         }
       }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const uint32_t lo = pack_bf16x2(acc[i][j][4 * q4] + bv[0], acc[i][j][4 * q4 + 1] + bv[1]);
+        const uint32_t hi =
+            pack_bf16x2(acc[i][j][4 * q4 + 2] + bv[2], acc[i][j][4 * q4 + 3] + bv[3]);
+        const int tt = 64 * wn + 32 * j + ql;   // token of the block
+        if (sec < 2) {
+          // [token][feature] rows of 256 bytes, 16-byte chunks swizzled by token
+          *reinterpret_cast<uint2*>(stage + tt * 256 + ((((fl >> 3) ^ tt) & 15) << 4) +
+                                    (hg << 3)) = make_uint2(lo, hi);
+        } else {
+          // [feature][token] rows of 512 bytes
+          uint16_t* col = reinterpret_cast<uint16_t*>(stage + fl * (BN * 2) + tt * 2);
+          col[0] = (uint16_t)lo;
+          col[BN] = (uint16_t)(lo >> 16);
+          col[2 * BN] = (uint16_t)hi;
+          col[3 * BN] = (uint16_t)(hi >> 16);
+        }
+      }
+    }
+  // the wave re-reads only what it wrote: LDS operations of one wave complete
+  // in order, and the wait keeps the compiler from moving the reads up
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+
+  int bad = 0;
+  if (sec < 2) {
+    const bool rot = p.rope != 0;
+    // 64 tokens x 16 chunks of 8 features: lane -> (token, chunk); the
+    // chunk c = lane % 16 is the same in every iteration, and with it the
+    // lane's 4 pairs, their axes and table rows
+    const int c = lane & 15;
+    int ax[4] = {0, 0, 0, 0}, rbq[4] = {0, 0, 0, 0};
+    if (rot) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        ax[q] = axis_of(p, 4 * c + q);
+        if (use_tab) rbq[q] = rbt[4 * c + q];
+      }
+    }
+#pragma unroll 2
+    for (int it = 0; it < 16; ++it) {
+      const int tk = 4 * it + (lane >> 4);
+      const int tt = 64 * wn + tk;
+      const int t = t0 + tt;
+      const int page = __shfl(pg, tk);   // every lane active here
+      if (t >= p.n_tok) continue;
+      uint4 v = *reinterpret_cast<const uint4*>(stage + tt * 256 + (((c ^ tt) & 15) << 4));
+      if (rot) {
+        const int4 pz = post[tt];
+        uint32_t* wv = reinterpret_cast<uint32_t*>(&v);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int pv = ax[q] == 0 ? pz.x : (ax[q] == 1 ? pz.y : pz.z);
+          const float2 cs =
+              use_tab ? tab[rbq[q] + pv] : rotary_factors(pv, p.pair_omega[4 * c + q]);
+          float y0, y1;
+          rotate_pair(__uint_as_float(wv[q] << 16), __uint_as_float(wv[q] & 0xffff0000u), cs,
+                      y0, y1);
+          wv[q] = pack_bf16x2(y0, y1);
+        }
+      }
+      if (sec == 0) {
+        *reinterpret_cast<uint4*>(p.q_out + (int64_t)t * p.q_stride + head * D + c * 8) = v;
+      } else {
+        const int L = p.dst_start + t;
+        if ((unsigned)page >= (unsigned)p.num_pages) {
+          bad = 1;
+          continue;
+        }
+        *reinterpret_cast<uint4*>(
+            p.k_pages + (((int64_t)page * p.heads + head) * ps + (L & (ps - 1))) * D + c * 8) = v;
+      }
+    }
+  } else {
+    // 128 features x 8 runs of 8 tokens: lane -> (feature, run)
+#pragma unroll 2
+    for (int it = 0; it < 16; ++it) {
+      const int idx = it * 64 + lane;
+      const int fr = idx >> 3, tt = 64 * wn + 8 * (idx & 7);
+      const int t = t0 + tt;
+      const int L = p.dst_start + t;
+      const char* src = stage + fr * (BN * 2) + tt * 2;
+      const int page = __shfl(pg, 8 * (idx & 7));   // every lane active here
+      if (t + 8 <= p.n_tok && (L & 7) == 0) {
+        // 8 consecutive tokens of one page (pages hold a multiple of 8)
+        if ((unsigned)page >= (unsigned)p.num_pages) {
+          bad = 1;
+          continue;
+        }
+        *reinterpret_cast<uint4*>(p.v_pages + (((int64_t)page * p.heads + head) * D + fr) * ps +
+                                  (L & (ps - 1))) = *reinterpret_cast<const uint4*>(src);
+      } else {
+        for (int u = 0; u < 8 && t + u < p.n_tok; ++u) {
+          const int Lu = L + u;
+          const int page = p.page_table[Lu >> p.ps_log2];
+          if ((unsigned)page >= (unsigned)p.num_pages) {
+            bad = 1;
+            continue;
+          }
+          p.v_pages[(((int64_t)page * p.heads + head) * D + fr) * ps + (Lu & (ps - 1))] =
+              reinterpret_cast<const uint16_t*>(src)[u];
+        }
+      }
+    }
   }
   if (bad) atomicOr(p.status, WF_STATUS_BAD_PAGE);
 }

@@ -6,6 +6,11 @@
 
 namespace wf {
 
+constexpr int kQkvBlockFeat = 256;  // output features per block (two heads of 128)
+constexpr int kQkvBlockTok = 256;   // tokens per block
+constexpr int kQkvFT = 4;           // feature tiles per XCD chunk
+constexpr int kQkvTT = 8;           // token tiles per XCD chunk
+
 struct QkvParams {
   const uint16_t* x;          // [n_tok] rows of [hidden] (bf16)
   const uint16_t* w;          // [3*H*D][hidden] (bf16), one row per output feature
@@ -19,12 +24,36 @@ struct QkvParams {
   int64_t x_stride, q_stride; // elements between rows
   int32_t n_tok, hidden, dst_start, heads, ps_log2, num_pages;
   int32_t tok_tiles;          // ceil(n_tok / 256)
-  int32_t feat_tiles;         // 128-feature tiles computed (2H without Q, 3H with)
-  int32_t sec0;               // section of the first tile: 0 (Q) or 1 (K)
+  int32_t feat_tiles;         // ceil(computed heads / 2); computed heads: 2H without Q, 3H with
+  int32_t sec0;               // section of the first computed head: 0 (Q) or 1 (K)
   int32_t rope;               // 0/1
-  int32_t pair_axis[kMaxPairs];
+  int32_t band0[4];           // first pair of the t, h, w sub-bands; band0[3] = D/2
   double pair_omega[kMaxPairs];
 };
+
+struct QkvTile {
+  int ftile, ttile;
+};
+
+// Block -> (feature tile, token tile).  The hardware deals consecutive
+// blocks to the 8 XCDs in turn; block b is renumbered so that every XCD
+// walks a contiguous run w of the work order (b >= 8 * (nb / 8): w = b).
+// The work order takes token tiles in groups of kQkvTT and, inside a group,
+// feature tiles in chunks of kQkvFT, token tile fastest: the blocks an XCD
+// runs at once form a kQkvFT x kQkvTT chunk of the output, whose weight and
+// hidden-state rows its L2 serves to several blocks each.
+__host__ __device__ inline QkvTile qkv_tile(int b, int nb, int feat_tiles, int tok_tiles) {
+  const int per = nb >> 3;
+  const int w = (b < (per << 3)) ? ((b & 7) * per + (b >> 3)) : b;
+  const int group_blocks = kQkvTT * feat_tiles;
+  const int g = w / group_blocks;
+  const int rem = w - g * group_blocks;
+  const int tt_in_g = (tok_tiles - g * kQkvTT < kQkvTT) ? tok_tiles - g * kQkvTT : kQkvTT;
+  const int chunk = rem / (kQkvFT * tt_in_g);
+  const int idx = rem - chunk * kQkvFT * tt_in_g;
+  const int f = idx / tt_in_g;
+  return QkvTile{chunk * kQkvFT + f, g * kQkvTT + (idx - f * tt_in_g)};
+}
 
 hipError_t launch_qkv_publish(const QkvParams& p, hipStream_t stream);
 

@@ -1,14 +1,17 @@
-// Host check of the attention work-item mapping (xcd_work_item and its
-// fallback xcd_run_item in wf_internal.h): for a grid of nb = query tiles
-// x heads blocks, the block -> item map must be a permutation of [0, nb),
-// so that every (head, group, query tile) is computed exactly once.
-// Exits non-zero and names the layout on the first failure.
+// Host check of the block -> work mappings: the attention work items
+// (xcd_work_item and its fallback xcd_run_item in wf_internal.h) for a grid
+// of nb = query tiles x heads blocks must be a permutation of [0, nb), so
+// that every (head, group, query tile) is computed exactly once; the fused
+// QKV projection's tiles (qkv_tile in wf_qkv.h) must cover every (feature
+// tile, token tile) of the grid exactly once.  Exits non-zero and names the
+// layout on the first failure.
 #include <algorithm>
 #include <cstdio>
 #include <random>
 #include <vector>
 
 #include "wf_internal.h"
+#include "wf_qkv.h"
 
 using wf::AttnParams;
 
@@ -36,8 +39,35 @@ static bool check(const std::vector<int>& tiles, int heads, bool run_only, int* 
   return true;
 }
 
+static bool check_qkv(int feat_tiles, int tok_tiles) {
+  const int nb = feat_tiles * tok_tiles;
+  std::vector<char> seen(nb, 0);
+  for (int b = 0; b < nb; ++b) {
+    const wf::QkvTile t = wf::qkv_tile(b, nb, feat_tiles, tok_tiles);
+    if (t.ftile < 0 || t.ftile >= feat_tiles || t.ttile < 0 || t.ttile >= tok_tiles ||
+        seen[t.ftile * tok_tiles + t.ttile]++) {
+      std::printf("qkv tiles not a permutation: %d feature x %d token tiles\n", feat_tiles,
+                  tok_tiles);
+      return false;
+    }
+  }
+  return true;
+}
+
 int main() {
   int fallback = 0, n = 0;
+  // fused QKV projection: every grid up to 64 x 40 tiles, and the 14B-like
+  // ticks (60 or 40 feature tiles over 92 or 211 token tiles)
+  for (int f = 1; f <= 64; ++f)
+    for (int t = 1; t <= 40; ++t) {
+      if (!check_qkv(f, t)) return 1;
+      ++n;
+    }
+  for (int f : {20, 30, 40, 60})
+    for (int t : {19, 92, 211}) {
+      if (!check_qkv(f, t)) return 1;
+      ++n;
+    }
   // the query tiles per slot of the five workload shapes
   const std::vector<std::pair<std::vector<int>, int>> shapes = {
       {{1, 1}, 2}, {{19, 19, 19, 19}, 12}, {{19, 19, 19, 19, 19}, 12},

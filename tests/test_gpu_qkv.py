@@ -87,16 +87,33 @@ CASES = {
     "ps64_plain": (2, 192, 130, 64, 64, False, False, False),
     "ps256_h3": (3, 384, 700, 256, 1000, True, True, True),
     "ps64_one_tile_no_q": (1, 64, 17, 64, 5, True, False, True),
+    "ps32_wide_positions": (2, 128, 300, 32, 64, True, True, "wide"),
+    "ps16_denormal_outputs": (1, 64, 80, 16, 0, False, True, "denormal"),
 }
 
 
-def draw(H, hidden, n, seed):
+def draw(H, hidden, n, seed, wide=False):
     g = torch.Generator().manual_seed(seed)
     x = torch.randn(n, hidden, generator=g).to(torch.bfloat16)
     w = (torch.randn(3 * H * 128, hidden, generator=g) / hidden ** 0.5).to(torch.bfloat16)
     b = (torch.randn(3 * H * 128, generator=g) * 0.1).to(torch.bfloat16)
-    pos = torch.stack([torch.arange(n) // 40, torch.arange(n) % 40 // 8, torch.arange(n) % 8],
-                      1).to(torch.int32)
+    if wide == "denormal":
+        # every output is one hidden state times 1 + 2^-7: x is a bfloat16
+        # denormal m * 2^-133, so the float32 product m (1 + 2^-7) 2^-133 is
+        # exact and its rounding to bfloat16 happens in the denormal range
+        # (m = 64 is a tie); the rotation then multiplies denormals
+        m = torch.randint(1, 128, (n, hidden), generator=g).to(torch.float64)
+        x = (m * 2.0 ** -133).to(torch.bfloat16)
+        w = torch.zeros(3 * H * 128, hidden, dtype=torch.float64)
+        w[torch.arange(3 * H * 128), torch.arange(3 * H * 128) % hidden] = 1 + 2.0 ** -7
+        w = w.to(torch.bfloat16)
+    if wide == "wide":
+        # positions spread over +-50000 per axis: far more (pair, position)
+        # combinations per 256-token block than the kernel's factor table holds
+        pos = torch.randint(-50000, 50000, (n, 3), generator=g).to(torch.int32)
+    else:
+        pos = torch.stack([torch.arange(n) // 40, torch.arange(n) % 40 // 8, torch.arange(n) % 8],
+                          1).to(torch.int32)
     return x, w, b, pos
 
 
@@ -104,7 +121,8 @@ def draw(H, hidden, n, seed):
 def test_qkv_publish_parity(name):
     H, hidden, n, ps, dst, use_bias, use_q, use_rope = CASES[name]
     print(f"\n[qkv] {name}", flush=True)
-    x, w, b, pos = draw(H, hidden, n, seed=hash(name) % 1000)
+    wide = use_rope if isinstance(use_rope, str) else False
+    x, w, b, pos = draw(H, hidden, n, seed=sum(map(ord, name)), wide=wide)
     n_log = (dst + n + ps - 1) // ps + 1
     rng = np.random.default_rng(7)
     table = rng.permutation(n_log + 2)[:n_log].astype(np.int32)
