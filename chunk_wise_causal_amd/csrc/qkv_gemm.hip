@@ -180,50 +180,58 @@ __device__ __forceinline__ void k_step(int kt, int ktiles, const char* lds, cons
   const char* nslot = lds + ((kt + 1) % NSL) * SLOT;
   const int kb = min(kt + NSL, ktiles - 1) * TK * 2;
   const uint32_t dst = wave_lds + (uint32_t)(kt % NSL) * SLOT;
+  // one load every 4 products, so that the CU's load path (about 64 bytes
+  // per clock, shared by the 8 waves) sees an even stream instead of a burst
+  // after the barrier; the 12 fragment reads of tile kt+1 go in between
   fence();
   mma<0>(cur, acc);
   fence();
   dma16<0>(wbase + kb, aoff[0], dst);
-  fence();
-  mma<1>(cur, acc);
-  fence();
-  dma16<8192>(wbase + kb, aoff[1], dst);
-  fence();
-  mma<2>(cur, acc);
-  fence();
-  dma16<A_BYTES>(xbase + kb, boff[0], dst);
-  fence();
-  mma<3>(cur, acc);
-  fence();
-  dma16<A_BYTES + 8192>(xbase + kb, boff[1], dst);
-  fence();
-  mma<4>(cur, acc);
   read_frag<0>(nxt, nslot, ra, rb, xo);
   read_frag<1>(nxt, nslot, ra, rb, xo);
   fence();
-  mma<5>(cur, acc);
+  mma<1>(cur, acc);
+  fence();
   read_frag<2>(nxt, nslot, ra, rb, xo);
   read_frag<3>(nxt, nslot, ra, rb, xo);
   fence();
-  mma<6>(cur, acc);
+  mma<2>(cur, acc);
+  fence();
   read_frag<4>(nxt, nslot, ra, rb, xo);
   read_frag<5>(nxt, nslot, ra, rb, xo);
   fence();
-  mma<7>(cur, acc);
+  mma<3>(cur, acc);
+  fence();
+  mma<4>(cur, acc);
+  fence();
+  dma16<8192>(wbase + kb, aoff[1], dst);
   read_frag<6>(nxt, nslot, ra, rb, xo);
   read_frag<7>(nxt, nslot, ra, rb, xo);
   fence();
-  mma<8>(cur, acc);
+  mma<5>(cur, acc);
+  fence();
   read_frag<8>(nxt, nslot, ra, rb, xo);
   read_frag<9>(nxt, nslot, ra, rb, xo);
   fence();
-  mma<9>(cur, acc);
+  mma<6>(cur, acc);
+  fence();
   read_frag<10>(nxt, nslot, ra, rb, xo);
   read_frag<11>(nxt, nslot, ra, rb, xo);
   fence();
+  mma<7>(cur, acc);
+  fence();
+  mma<8>(cur, acc);
+  fence();
+  dma16<A_BYTES>(xbase + kb, boff[0], dst);
+  fence();
+  mma<9>(cur, acc);
   mma<10>(cur, acc);
   mma<11>(cur, acc);
+  fence();
   mma<12>(cur, acc);
+  fence();
+  dma16<A_BYTES + 8192>(xbase + kb, boff[1], dst);
+  fence();
   mma<13>(cur, acc);
   mma<14>(cur, acc);
   mma<15>(cur, acc);

@@ -8,8 +8,11 @@ namespace wf {
 
 constexpr int kQkvBlockFeat = 256;  // output features per block (two heads of 128)
 constexpr int kQkvBlockTok = 256;   // tokens per block
-constexpr int kQkvFT = 4;           // feature tiles per XCD chunk
-constexpr int kQkvTT = 8;           // token tiles per XCD chunk
+#ifndef WF_QKV_FT
+#define WF_QKV_FT 8
+#endif
+constexpr int kQkvFT = WF_QKV_FT;   // feature tiles per XCD chunk
+constexpr int kQkvTT = 32 / kQkvFT; // token tiles per XCD chunk (32 blocks, one per CU)
 
 struct QkvParams {
   const uint16_t* x;          // [n_tok] rows of [hidden] (bf16)
@@ -36,15 +39,26 @@ struct QkvTile {
 };
 
 // Block -> (feature tile, token tile).  The hardware deals consecutive
-// blocks to the 8 XCDs in turn; block b is renumbered so that every XCD
-// walks a contiguous run w of the work order (b >= 8 * (nb / 8): w = b).
+// blocks to the 8 XCDs in turn, so block b runs on XCD x = b % 8 as the
+// k-th block of that XCD, k = b / 8.  The work order is cut into chunks of
+// 32 (kQkvFT feature tiles x kQkvTT token tiles): round r gives XCD x the
+// chunk 8r + x, its 32 blocks k = 32r .. 32r+31 at once, so the blocks an
+// XCD runs together share weight and hidden-state rows in its L2, and the 8
+// XCDs work on 8 neighbouring chunks (the same token rows) at the same
+// time, which keeps the rows they miss in the L2 few enough for the
+// memory-side cache.  The blocks of the last, partial round and those past
+// 8 * (nb / 8) take the rest of the work order in turn.
 // The work order takes token tiles in groups of kQkvTT and, inside a group,
-// feature tiles in chunks of kQkvFT, token tile fastest: the blocks an XCD
-// runs at once form a kQkvFT x kQkvTT chunk of the output, whose weight and
-// hidden-state rows its L2 serves to several blocks each.
+// feature tiles in chunks of kQkvFT, token tile fastest.
 __host__ __device__ inline QkvTile qkv_tile(int b, int nb, int feat_tiles, int tok_tiles) {
-  const int per = nb >> 3;
-  const int w = (b < (per << 3)) ? ((b & 7) * per + (b >> 3)) : b;
+  const int per = nb >> 3;            // blocks per XCD in the dealt part
+  const int rounds = per >> 5;        // full rounds of 32 blocks per XCD
+  int w = b;
+  if (b < (per << 3)) {
+    const int x = b & 7, k = b >> 3;
+    w = (k < (rounds << 5)) ? (((k >> 5) << 8) + (x << 5) + (k & 31))
+                            : ((rounds << 8) + ((k - (rounds << 5)) << 3) + x);
+  }
   const int group_blocks = kQkvTT * feat_tiles;
   const int g = w / group_blocks;
   const int rem = w - g * group_blocks;
