@@ -237,6 +237,49 @@ __device__ __forceinline__ void k_step(int kt, int ktiles, const char* lds, cons
   mma<15>(cur, acc);
 }
 
+// Phase 2 of the epilogue for a Q or K head, iteration it: the lane's
+// 16-byte chunk c of token 64 wn + 4 it + lane / 16 is read from the stage,
+// rotated (MODE 0: no rotation, 1: factors from the block's table, 2:
+// factors evaluated per element) and stored to its Q row or K page row.
+template <int MODE>
+__device__ __forceinline__ void qk_store(const QkvParams& p, int it, int lane, int wn, int t0,
+                                         int pg, int c, const int* ax, const int* rbq,
+                                         const char* stage, const int4* post,
+                                         const float2* tab, int sec, int head, int ps,
+                                         int& bad) {
+  const int tk = 4 * it + (lane >> 4);
+  const int tt = 64 * wn + tk;
+  const int t = t0 + tt;
+  const int page = __shfl(pg, tk);   // every lane active here
+  if (t >= p.n_tok) return;
+  uint4 v = *reinterpret_cast<const uint4*>(stage + tt * 256 + (((c ^ tt) & 15) << 4));
+  if (MODE != 0) {
+    const int4 pz = post[tt];
+    uint32_t* wv = reinterpret_cast<uint32_t*>(&v);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int pv = ax[q] == 0 ? pz.x : (ax[q] == 1 ? pz.y : pz.z);
+      const float2 cs =
+          MODE == 1 ? tab[rbq[q] + pv] : rotary_factors(pv, p.pair_omega[4 * c + q]);
+      float y0, y1;
+      rotate_pair(__uint_as_float(wv[q] << 16), __uint_as_float(wv[q] & 0xffff0000u), cs, y0,
+                  y1);
+      wv[q] = pack_bf16x2(y0, y1);
+    }
+  }
+  if (sec == 0) {
+    *reinterpret_cast<uint4*>(p.q_out + (int64_t)t * p.q_stride + head * D + c * 8) = v;
+  } else {
+    const int L = p.dst_start + t;
+    if ((unsigned)page >= (unsigned)p.num_pages) {
+      bad = 1;
+      return;
+    }
+    *reinterpret_cast<uint4*>(p.k_pages + (((int64_t)page * p.heads + head) * ps + (L & (ps - 1))) * D +
+                              c * 8) = v;
+  }
+}
+
 __global__ __attribute__((amdgpu_flat_work_group_size(NTH, NTH)))
 void qkv_gemm_publish(const QkvParams p) {
   __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
@@ -476,43 +519,24 @@ void qkv_gemm_publish(const QkvParams p) {
         if (use_tab) rbq[q] = rbt[4 * c + q];
       }
     }
-#pragma unroll 2
-    for (int it = 0; it < 16; ++it) {
-      const int tk = 4 * it + (lane >> 4);
-      const int tt = 64 * wn + tk;
-      const int t = t0 + tt;
-      const int page = __shfl(pg, tk);   // every lane active here
-      if (t >= p.n_tok) continue;
-      uint4 v = *reinterpret_cast<const uint4*>(stage + tt * 256 + (((c ^ tt) & 15) << 4));
-      if (rot) {
-        const int4 pz = post[tt];
-        uint32_t* wv = reinterpret_cast<uint32_t*>(&v);
+    // the rotation mode picks one of three copies of the loop: unrolled for
+    // no rotation and for table factors, rolled for per-element factors
+    if (!rot) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int pv = ax[q] == 0 ? pz.x : (ax[q] == 1 ? pz.y : pz.z);
-          const float2 cs =
-              use_tab ? tab[rbq[q] + pv] : rotary_factors(pv, p.pair_omega[4 * c + q]);
-          float y0, y1;
-          rotate_pair(__uint_as_float(wv[q] << 16), __uint_as_float(wv[q] & 0xffff0000u), cs,
-                      y0, y1);
-          wv[q] = pack_bf16x2(y0, y1);
-        }
-      }
-      if (sec == 0) {
-        *reinterpret_cast<uint4*>(p.q_out + (int64_t)t * p.q_stride + head * D + c * 8) = v;
-      } else {
-        const int L = p.dst_start + t;
-        if ((unsigned)page >= (unsigned)p.num_pages) {
-          bad = 1;
-          continue;
-        }
-        *reinterpret_cast<uint4*>(
-            p.k_pages + (((int64_t)page * p.heads + head) * ps + (L & (ps - 1))) * D + c * 8) = v;
-      }
+      for (int it = 0; it < 16; ++it)
+        qk_store<0>(p, it, lane, wn, t0, pg, c, ax, rbq, stage, post, tab, sec, head, ps, bad);
+    } else if (use_tab) {
+#pragma unroll
+      for (int it = 0; it < 16; ++it)
+        qk_store<1>(p, it, lane, wn, t0, pg, c, ax, rbq, stage, post, tab, sec, head, ps, bad);
+    } else {
+#pragma unroll 1
+      for (int it = 0; it < 16; ++it)
+        qk_store<2>(p, it, lane, wn, t0, pg, c, ax, rbq, stage, post, tab, sec, head, ps, bad);
     }
   } else {
     // 128 features x 8 runs of 8 tokens: lane -> (feature, run)
-#pragma unroll 2
+#pragma unroll
     for (int it = 0; it < 16; ++it) {
       const int idx = it * 64 + lane;
       const int fr = idx >> 3, tt = 64 * wn + 8 * (idx & 7);
