@@ -1,767 +1,179 @@
 // wf_chunk_attn, bfloat16: slot-masked flash-attention forward over the paged
-// K/V pool on CDNA4 matrix cores.
+// K/V pool on CDNA4 matrix cores ("Wave Forcing: Towards Speed-of-Light
+// Streaming Video Generation", §3.1).  The walk, masks, softmax, P V and
+// pipeline are the shared core (attn_core.h); this file supplies the
+// bfloat16 score product:
 //
-// "Wave Forcing: Towards Speed-of-Light Streaming Video Generation", §3.1:
-// a query of denoising slot s attends to the anchor, the clean history, the
-// live store and every slot j >= s (itself included, with full attention
-// inside the chunk).  The host turns that rule into a list of merged visible
-// key ranges per slot; this kernel walks only the key tiles those ranges
-// touch, so tiles the mask removes entirely are never loaded or multiplied.
+//   S^T = K Q^T   v_mfma_f32_32x32x16_bf16, A = K rows from LDS (bf16 pages
+//                 [H][ps][D], one 64-key tile per slot), B = Q^T held in
+//                 registers for the whole kernel, D / 16 k-steps per 32x32
+//                 block.
 //
-// Work unit: one block = (head, slot, 256-row query tile), 8 waves of 64
-// lanes, each wave owning 32 query rows; every K/V tile brought into LDS
-// serves all 256 rows, which halves the L2 -> CU traffic of 128-row tiles.
-// Per 64-key tile:
-//   S^T = K Q^T   v_mfma_f32_32x32x16_bf16, A = K rows from LDS, B = Q^T held
-//                 in registers for the whole kernel.  The transposed product
-//                 puts one query in every lane (lanes l and l+32 share it),
-//                 so row max / row sum need a single cross-half exchange.
-//   mask          only on tiles cut by a range boundary: keys outside the
-//                 range become -inf; their K/V rows are never read from HBM
-//                 (filled in LDS: K with NaN, which the row max skips, V with
-//                 zeros), so stale or NaN memory cannot leak.
-//   softmax       online, base 2, with the running max raised only when a
-//                 row's tile max exceeds it by more than 2^8 (the exact
-//                 result is unchanged: numerator and denominator share the
-//                 stale max, and 2^8 keeps every term finite).  The max of
-//                 tile j+1 is taken while O += P(j) V(j) runs, so the
-//                 probabilities of a tile never wait for a reduction.  The
-//                 denominator sums the bf16-rounded probabilities that
-//                 multiply V (v_dot2 against 1.0), so the weights applied to
-//                 V are normalized exactly.
-//   O^T += V^T P^T  A = V^T read from the d-major V pages via LDS, B = P^T
-//                 straight from the S^T accumulators: the K rows of S^T are
-//                 loaded in the order sigma(i) (bits 2 and 3 of the row index
-//                 swapped) so that each lane's 8 probabilities of a k-step
-//                 are 8 consecutive keys, matching a 16-byte V^T read.
-//
-// Pipeline: a ring of four LDS slots each for K and V, filled by direct
-// global->LDS loads (global_load_lds_dwordx4) four and two tiles ahead.  Per
-// tile, S(j+1) = K(j+1) Q^T is issued while the softmax of tile j runs, and
-// the max of S(j+1) is taken while O += P(j) V(j) runs.  Half of the waves
-// run half a tile behind the other half (one of each on every SIMD), so the
-// vector work of one overlaps the matrix work of the other.  One barrier per
-// tile.  Tiles cut by a range boundary, spread over several pages or naming
-// a bad page take a register path that fills what lies outside the window.
-//
-// LDS layout: 16-byte chunks XOR-swizzled by row so that the A-operand reads
-// of 8 (or 16) consecutive lanes hit distinct banks: K chunk c of row r sits
-// at column c ^ kswz(r); V^T chunk c of feature row d at column c ^ vswz(d).
-//
-// Block ids are remapped so that each XCD (blocks are dealt round-robin over
-// the 8 XCDs) receives a contiguous run of the work list: the query tiles of
-// one head and slot then share that XCD's L2 while streaming the same keys.
-#include "../../include/wf.h"
-#include "wf_internal.h"
+// LDS layout of a K slot: 16-byte chunks XOR-swizzled by row so that the
+// A-operand reads of 8 (or 16) consecutive lanes hit distinct banks: chunk c
+// of row r sits at column c ^ kswz(r).
+#include "attn_core.h"
 
 namespace wf {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+using namespace attn;
 
-constexpr int NW = 8;       // waves per block, 32 query rows each
-constexpr int BM = 32 * NW; // query rows per block
-constexpr int BN = 64;      // keys per tile
-constexpr int NT = 64 * NW; // threads per block
-constexpr int LT = NT / 2;  // threads that issue the K/V tile loads (waves 0..NW/2-1)
-constexpr float kRescaleSlack = 8.0f;   // log2 units
-constexpr float kLn2 = 0.6931471805599453f;
-
-__device__ __forceinline__ float xhalf_max(float x) {
-  auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-}
-
-__device__ __forceinline__ float xhalf_sum(float x) {
-  auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-}
-
-// row of the K tile feeding S^T row i: bits 2 and 3 swapped
-__device__ __forceinline__ int sigma(int i) {
-  return (i & 0x13) | ((i & 4) << 1) | ((i & 8) >> 1);
-}
-
-// column swizzles (16-byte chunk units)
+// K column swizzle (16-byte chunk units)
 template <int D>
 __device__ __forceinline__ int kswz(int r) {
   return ((((r & 7) ^ ((r >> 1) & 4)) | (r & 8)) & (D / 8 - 1));
 }
-__device__ __forceinline__ int vswz(int d) { return (d & 7) ^ ((d >> 3) & 1); }
 
-// Physical page for a page-table entry, or -1 (and `bad` set) for an entry
-// outside the pool; integer arithmetic only, so that a uniform entry stays
-// in scalar registers.  The status word is written once, after the key loop.
-__device__ __forceinline__ int check_page(const AttnParams& p, int page, int& bad) {
-  const int out = (unsigned)page >= (unsigned)p.num_pages;
-  bad |= out;
-  return out ? -1 : page;
-}
+struct ScoreBf16 {
+  struct Extra {};
+  template <int D> static constexpr uint32_t KSLOT = BN * D * 2;   // bytes of one K slot
+  template <int D> static constexpr uint32_t XSLOT = 0;            // no extra slots
+  template <int D> static constexpr int PER_K = BN * (D / 8) / LT; // 16-byte chunks per thread
+  template <int D> static constexpr int KDMAS = PER_K<D>;
 
-// Per-lane lookup (register path: the token may differ between lanes).
-__device__ __forceinline__ int lookup_page(const AttnParams& p, int L, int& bad) {
-  return check_page(p, p.page_table[L >> p.ps_log2], bad);
-}
-
-// Wave-uniform page-table read through the constant address space: the
-// table is read-only for the kernel, so the compiler emits a scalar load it
-// can issue early and wait for exactly.  (A generic read becomes a vector
-// load, and consuming one needs vmcnt(0), which would drain every in-flight
-// tile load of the ring.)
-typedef const __attribute__((address_space(4))) int32_t* const_table_ptr;
-
-__device__ __forceinline__ int table_entry(const AttnParams& p, int logical_page) {
-  return ((const_table_ptr)p.page_table)[logical_page];
-}
-
-// Position of the tile walk over the merged visible ranges of one group:
-// the tile's first key kt, its range [rlo, rhi) and the physical page of
-// the tile (pages of >= BN keys), read a step before the tile is loaded.
-struct Walk {
-  int ri;     // current range; == rng1 once past the last tile
-  int kt;
-  int rlo;
-  int rhi;
-  int page;
-};
-
-// One key tile as the loads and the mask see it, in three scalar registers:
-// ktc = first key | 1 when the tile is cut by its range (ktc < 0: past the
-// end of the walk), ri = its range, page = its physical page (-1 when the
-// tile spans several pages or its page entry is bad).
-struct Tile {
-  int ktc;
-  int ri;
-  int page;
-};
-
-// BP: pages hold at least BN keys, so a 64-aligned tile lies in one page
-// (otherwise every tile takes the register path, with per-lane lookups).
-template <bool BP>
-__device__ __forceinline__ void walk_page(const AttnParams& p, Walk& w) {
-  if (BP) w.page = table_entry(p, w.kt >> p.ps_log2);
-}
-
-template <bool BP>
-__device__ __forceinline__ Walk walk_first(const AttnParams& p, int rng0) {
-  const int2 r = p.ranges[rng0];
-  Walk w{rng0, r.x & ~(BN - 1), r.x, r.y, -1};
-  walk_page<BP>(p, w);
-  return w;
-}
-
-template <bool BP>
-__device__ __forceinline__ void walk_next(const AttnParams& p, int rng1, Walk& w) {
-  w.kt += BN;
-  if (w.kt >= w.rhi) {
-    if (++w.ri >= rng1) return;
-    const int2 r = p.ranges[w.ri];
-    w.rlo = r.x;
-    w.rhi = r.y;
-    w.kt = r.x & ~(BN - 1);
-  }
-  walk_page<BP>(p, w);
-}
-
-// The tile at the walk position; its page entry is checked here, once.
-// The cut flag is integer arithmetic (sign bits), not a boolean, so that it
-// stays in scalar registers.
-template <bool BP>
-__device__ __forceinline__ Tile walk_tile(const AttnParams& p, int rng1, const Walk& w,
-                                          int& bad) {
-  if (w.ri >= rng1) return Tile{-1, 0, -1};
-  const int page = BP ? check_page(p, w.page, bad) : -1;
-  const int cut = (int)(((uint32_t)(w.kt - w.rlo) | (uint32_t)(w.rhi - (w.kt + BN))) >> 31);
-  return Tile{w.kt | cut, w.ri, page};
-}
-
-__device__ __forceinline__ int tile_kt(const Tile& t) { return t.ktc & ~(BN - 1); }
-__device__ __forceinline__ bool tile_cut(const Tile& t) { return t.ktc & 1; }
-
-// visible keys [lo, hi) of a tile
-__device__ __forceinline__ void tile_window(const AttnParams& p, const Tile& t, int& lo,
-                                            int& hi) {
-  const int2 r = p.ranges[t.ri];
-  lo = max(tile_kt(t), r.x);
-  hi = min(tile_kt(t) + BN, r.y);
-}
-
-// every key of the tile visible and on one good page: the direct-load path
-__device__ __forceinline__ bool tile_full(const Tile& t) {
-  return ((t.page >> 31) | (t.ktc & 1)) == 0;
-}
-
-// Block-constant addressing of the loads, which the first LT threads issue
-// (the waves that run ahead; see Loop).  The K page [H][ps][D] and the V
-// page [H][D][ps] of one head have the same size, so one page stride and one
-// per-head offset serve both.
-template <int D>
-struct LoadCtx {
-  static constexpr int PER_K = BN * (D / 8) / LT;   // 16-byte chunks per thread
-  static constexpr int PER_V = D * (BN / 8) / LT;
-  const char* k_head;       // K pages + head offset (bytes)
-  const char* v_head;
-  int64_t page_bytes;
-  uint32_t koff[PER_K];     // per-lane byte offsets of this thread's chunks
-  uint32_t voff[PER_V];
-  uint32_t wave_lds;        // LDS byte address of this wave's first chunk
-};
-
-// Direct global->LDS load, 16 bytes per lane (global_load_lds_dwordx4, the
-// scalar-base form): lane i writes LDS bytes [M0 + 16 i, +16) with
-// M0 = wave_lds + OFF.  Issued as inline assembly so that the compiler does
-// not model it: with this LDS-DMA form in the loop its wait bookkeeping
-// drains every later LDS read with lgkmcnt(0), which serializes the
-// A-operand fragment reads.  The caller's explicit vmcnt waits track
-// completion.  The wait states cover an SGPR base written by a VALU
-// instruction just before (a memory instruction reading it needs 5) and the
-// M0 write read by the LDS-DMA load (1).
-template <uint32_t OFF>
-__device__ __forceinline__ void dma16(const char* sbase, uint32_t voff, uint32_t wave_lds) {
-  asm volatile(
-      "s_nop 4\n\t"
-      "s_add_u32 m0, %2, %3\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %0, %1"
-      :
-      : "v"(voff), "s"(sbase), "s"(wave_lds), "i"(OFF)
-      : "memory", "m0", "scc");
-}
-
-// The PER chunks of one thread: chunk i goes to this wave's 1 KB run
-// i*LT/64 runs further on.
-template <uint32_t SLOT, int I, int PER>
-__device__ __forceinline__ void dma_chunks(const char* base, const uint32_t* off,
-                                           uint32_t wave_lds) {
-  if constexpr (I < PER) {
-    dma16<SLOT + I * (LT / 64) * 1024>(base, off[I], wave_lds);
-    dma_chunks<SLOT, I + 1, PER>(base, off, wave_lds);
-  }
-}
-
-// ---- global -> LDS: the K tile [BN][D] of one head -------------------------
-// A full tile goes by direct loads (PER_K per thread, left in flight).  Any
-// other tile takes the register path, and a tile past the end of the walk
-// loads nothing; both end with every older vector load complete, so a step
-// never has more than its own direct loads outstanding.
-template <int D, bool BP, uint32_t SLOT>
-__device__ __forceinline__ void load_k(const AttnParams& p, const LoadCtx<D>& lc, int head,
-                                       const Tile& t, uint16_t* __restrict__ lds, int& bad) {
-  constexpr int CPR = D / 8;   // chunks per K row
-  constexpr int PER = LoadCtx<D>::PER_K;
-  const int ps = 1 << p.ps_log2;
-  if (tile_full(t)) {
-    const char* base = lc.k_head + (int64_t)t.page * lc.page_bytes +
-                       (int64_t)(tile_kt(t) & (ps - 1)) * (D * 2);
-    dma_chunks<SLOT, 0, PER>(base, lc.koff, lc.wave_lds);
-    return;
-  }
-  if (t.ktc >= 0) {
-    // rare (tile cut by a range boundary, spread over several pages, or on a
-    // bad page): one chunk at a time, to keep register pressure off the hot
-    // loop.  Rows outside the window hold bf16 quiet NaNs: their scores are
-    // NaN, which the row max skips (IEEE maxNum), and the mask sets them to
-    // -inf before any exponential, so the max of a cut tile is exact.
-    const int tid = threadIdx.x;
-    const uint16_t* __restrict__ kpg = static_cast<const uint16_t*>(p.k_pages);
-    uint16_t* kbuf = lds + SLOT / 2;
-    const uint4 nan8 = make_uint4(0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u);
-    const uint4 zero = make_uint4(0, 0, 0, 0);
-    int lo, hi;
-    tile_window(p, t, lo, hi);
-#pragma unroll 1
-    for (int i = 0; i < PER; ++i) {
-      const int q = i * LT + tid;
-      const int r = q / CPR, col = (q % CPR) ^ kswz<D>(r);
-      const int L = tile_kt(t) + r;
-      uint4 val = nan8;
-      if (L >= lo && L < hi) {
-        const int page = BP ? t.page : lookup_page(p, L, bad);
-        val = zero;
-        if (page >= 0)
-          val = *reinterpret_cast<const uint4*>(
-              kpg + (((int64_t)page * p.heads + head) * ps + (L & (ps - 1))) * D + col * 8);
-      }
-      *reinterpret_cast<uint4*>(kbuf + q * 8) = val;
-    }
-  }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-}
-
-// ---- global -> LDS: the V^T tile [D][BN] of one head -----------------------
-// Same contract as load_k.
-template <int D, bool BP, uint32_t SLOT>
-__device__ __forceinline__ void load_v(const AttnParams& p, const LoadCtx<D>& lc, int head,
-                                       const Tile& t, uint16_t* __restrict__ lds, int& bad) {
-  constexpr int PER = LoadCtx<D>::PER_V;
-  const int ps = 1 << p.ps_log2;
-  if (tile_full(t)) {
-    const char* base =
-        lc.v_head + (int64_t)t.page * lc.page_bytes + (int64_t)(tile_kt(t) & (ps - 1)) * 2;
-    dma_chunks<SLOT, 0, PER>(base, lc.voff, lc.wave_lds);
-    return;
-  }
-  if (t.ktc >= 0) {
-    const int tid = threadIdx.x;
-    const uint16_t* __restrict__ vpg = static_cast<const uint16_t*>(p.v_pages);
-    uint16_t* vbuf = lds + SLOT / 2;
-    const uint4 zero = make_uint4(0, 0, 0, 0);
-    int lo, hi;
-    tile_window(p, t, lo, hi);
-#pragma unroll 1
-    for (int i = 0; i < PER; ++i) {
-      const int q = i * LT + tid;
-      const int d = q >> 3, col = (q & 7) ^ vswz(d);
-      const int L = tile_kt(t) + col * 8;   // first of the chunk's 8 keys
-      uint4 val = zero;
-      if (L + 8 > lo && L < hi) {
-        // an 8-key run never crosses a page (page_size >= 16, runs 8-aligned)
-        const int page = BP ? t.page : lookup_page(p, max(L, lo), bad);
-        if (page >= 0) {
-          val = *reinterpret_cast<const uint4*>(
-              vpg + (((int64_t)page * p.heads + head) * D + d) * ps + (L & (ps - 1)));
-          if (L < lo || L + 8 > hi) {
-            uint16_t* e = reinterpret_cast<uint16_t*>(&val);
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-              if (L + j < lo || L + j >= hi) e[j] = 0;
-          }
-        }
-      }
-      *reinterpret_cast<uint4*>(vbuf + q * 8) = val;
-    }
-  }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-}
-
-template <int D>
-struct Frag {
-  static constexpr int DK = D / 16;   // k-steps of S^T = K Q^T
-  static constexpr int DB = D / 32;   // 32-wide d blocks of O^T
-  static constexpr int SB = BN / 32;  // 32-key blocks of S^T
-  static constexpr int PK = BN / 16;  // k-steps of O^T += V^T P^T
-};
-
-// S^T of one tile: s[sb] for keys 32sb.. of the K slot
-template <int D>
-__device__ __forceinline__ void qk(const uint16_t* __restrict__ kbuf, const int* kaddr,
-                                   const bf16x8* qf, f32x16* s) {
-#pragma unroll
-  for (int sb = 0; sb < Frag<D>::SB; ++sb) {
-    s[sb] = f32x16{};
-#pragma unroll
-    for (int i = 0; i < Frag<D>::DK; ++i) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(kbuf + kaddr[i] + 32 * sb * D);
-      s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[i], s[sb], 0, 0, 0);
-    }
-  }
-}
-
-// Row max of a score tile in log2 units, scaled by sl2 (both halves of the
-// row combined).
-template <int D>
-__device__ __forceinline__ float tile_max(const f32x16* s, float sl2) {
-  float mx = -INFINITY;
-#pragma unroll
-  for (int sb = 0; sb < Frag<D>::SB; ++sb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sb][r]);
-  return xhalf_max(mx) * sl2;
-}
-
-// bf16 probabilities of one tile for running max m, and their sum (over the
-// rounded values, via v_dot2 against 1.0)
-template <int D>
-__device__ __forceinline__ void probs(const f32x16* s, float sl2, float m, bf16x8* pb,
-                                      float* lsum) {
-  const float neg_m = -m;
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-  lsum[0] = 0.f;
-  lsum[1] = 0.f;
-#pragma unroll
-  for (int t = 0; t < Frag<D>::PK; ++t) {
-    uint32_t pk[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const f32x2 x = {__builtin_amdgcn_exp2f(fmaf(s[t >> 1][8 * (t & 1) + 2 * j], sl2, neg_m)),
-                       __builtin_amdgcn_exp2f(fmaf(s[t >> 1][8 * (t & 1) + 2 * j + 1], sl2, neg_m))};
-      const bf16x2 b = __builtin_convertvector(x, bf16x2);
-      pk[j] = __builtin_bit_cast(uint32_t, b);
-      lsum[j & 1] = __builtin_amdgcn_fdot2_f32_bf16(b, ones, lsum[j & 1], false);
-    }
-    pb[t] = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
-  }
-}
-
-template <int D>
-__device__ __forceinline__ void pv(const uint16_t* __restrict__ vbuf, const int* vaddr,
-                                   const bf16x8* pb, f32x16* o) {
-#pragma unroll
-  for (int t = 0; t < Frag<D>::PK; ++t)
-#pragma unroll
-    for (int db = 0; db < Frag<D>::DB; ++db) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(vbuf + vaddr[t] + 32 * db * BN);
-      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[t], o[db], 0, 0, 0);
-    }
-}
-
-// Scheduling hint for the block of O += P(j) V(j) and the max of S(j+1):
-// V^T fragment reads run a few products ahead and each MFMA is followed by
-// one vector instruction of the max.
-template <int D>
-__device__ __forceinline__ void interleave_pv_max() {
-  constexpr int NM = Frag<D>::PK * Frag<D>::DB;   // MFMAs of the product
-  constexpr int AHEAD = 3;
-#pragma unroll
-  for (int k = 0; k < AHEAD; ++k) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-#pragma unroll
-  for (int k = 0; k < NM; ++k) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);
-    if (k + AHEAD < NM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-  }
-}
-
-// Instruction-scheduling hint for the block that issues the S(j+1) MFMAs and
-// the softmax of tile j: K reads run a few ahead, and every MFMA is followed
-// by a share of the vector work (the tile's 32 exponentials and about 64
-// other instructions over 16 MFMAs), so the matrix pipe and the VALU run
-// together.  The grouping counts the exponential as a transcendental (mask
-// 0x400), not as a plain vector instruction (0x002): a group that names only
-// the latter leaves the exponentials to bunch behind the first MFMAs.  Three
-// of each per MFMA (the exponentials done by the eleventh MFMA, the rest of
-// the vector work trailing) measured 3 % faster than an even two and four.
-template <int D>
-__device__ __forceinline__ void interleave_qk_softmax() {
-  constexpr int NM = Frag<D>::SB * Frag<D>::DK;   // MFMAs of S(j+1)
-  constexpr int AHEAD = 3;
-  constexpr int TPM = 3;                           // exponentials per MFMA
-  constexpr int VPM = 3;                           // other VALU per MFMA
-#pragma unroll
-  for (int k = 0; k < AHEAD; ++k) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-#pragma unroll
-  for (int k = 0; k < NM; ++k) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x400, TPM, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);
-    if (k + AHEAD < NM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-  }
-}
-
-// Keys of a tile cut by a range boundary that lie outside [w_lo, w_hi) get
-// score -inf (their K/V rows were zero-filled, never read from memory).
-template <int D>
-__device__ __forceinline__ void mask_tile(f32x16* s, int kt, int w_lo, int w_hi, int hg) {
-  // register r of block sb holds key kt + 8hg + c with c = 32sb + 16(r/8) + r%8;
-  // it is visible iff c - lo lies in [0, hi - lo) (one unsigned compare)
-  const int lo = w_lo - (kt + 8 * hg);
-  const unsigned span = (unsigned)(w_hi - w_lo);
-#pragma unroll
-  for (int sb = 0; sb < Frag<D>::SB; ++sb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int c = 32 * sb + 16 * (r >> 3) + (r & 7);
-      if ((unsigned)(c - lo) >= span) s[sb][r] = -INFINITY;
-    }
-}
-
-// First half of tile j: S(j+1) = K(j+1) Q^T is issued while the softmax of
-// S(j) runs, producing the bf16 probabilities pb of tile j.  The running max
-// already bounds tile j (it was raised, if needed, while the previous tile's
-// product ran), so the probabilities are at most 2^kRescaleSlack and need no
-// max of their own: one straight-line block of MFMAs and vector work.
-template <int D>
-__device__ __forceinline__ void softmax_qk(const uint16_t* __restrict__ kb_next, const int* kaddr,
-                                           const bf16x8* qf, const f32x16* s_cur, f32x16* s_nxt,
-                                           float m_run, float* l_acc, float sl2, bf16x8* pb) {
-  qk<D>(kb_next, kaddr, qf, s_nxt);
-  float lsum[2];
-  probs<D>(s_cur, sl2, m_run, pb, lsum);
-#pragma unroll
-  for (int t = 0; t < Frag<D>::PK; ++t) asm volatile("" ::"v"(pb[t]));
-  asm volatile("" ::"v"(lsum[0]), "v"(lsum[1]));
-  interleave_qk_softmax<D>();
-  l_acc[0] += lsum[0];
-  l_acc[1] += lsum[1];
-}
-
-// Second half of tile j: O += P(j) V(j) while the max of S(j+1) is taken.
-// The running max is raised (wave-uniformly) only when some row's max
-// exceeds it by more than the slack; the caller then rescales O and l.
-template <int D>
-__device__ __forceinline__ bool pv_max(const uint16_t* __restrict__ vbuf, const int* vaddr,
-                                       const bf16x8* pb, f32x16* o, const f32x16* s_nxt,
-                                       float m_run, float sl2, float& m_new) {
-  pv<D>(vbuf, vaddr, pb, o);
-  const float mt = tile_max<D>(s_nxt, sl2);
-  interleave_pv_max<D>();
-  m_new = fmaxf(m_run, mt);
-  return __builtin_amdgcn_ballot_w64(mt > m_run + kRescaleSlack) != 0;
-}
-
-// Raise the running max to m_new: O and l scale by 2^(m_run - m_new).
-template <int D>
-__device__ __forceinline__ void rescale(f32x16* o, float* l_acc, float& m_run, float m_new) {
-  const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-  l_acc[0] *= alpha;
-  l_acc[1] *= alpha;
-#pragma unroll
-  for (int i = 0; i < Frag<D>::DB; ++i) o[i] *= alpha;
-  m_run = m_new;
-}
-
-// Ring of NS = 4 LDS slots for K and 4 for V, and two wave groups half a
-// tile apart.  Per tile j every wave runs [S(j+1) + softmax(j)] then
-// [O += P(j) V(j) + max of S(j+1)]; waves 0..NW/2-1 ("leading") take the
-// step's barrier after the second half, waves NW/2.. ("lagging") before it,
-// carrying P(j) in registers across the barrier.  Between two barriers a
-// leading wave thus runs softmax(j) then P(j) V(j) while a lagging wave runs
-// P(j-1) V(j-1) then softmax(j); the two waves sharing a SIMD are one of
-// each group, so while one issues the softmax's vector work the other keeps
-// the matrix pipe busy.
-// At tile j the slots hold K(j+1..j+4) and V(j-1..j+2); step j issues
-// K(j+4) into the slot of K(j) and V(j+2) into the slot of V(j-2), both read
-// by every wave before the previous barrier.  Only the leading waves issue
-// loads: they finish their half-tiles early and would otherwise idle at the
-// barrier, while the lagging waves' softmax is the critical path.  The
-// barrier of step j must publish K(j+2) and V(j+1), issued in earlier steps:
-// each loading wave waits until no more than this step's direct loads are
-// outstanding (vector loads complete in order), then the barrier publishes
-// them to all waves.
-// The walk runs once per step, four tiles ahead (for K); the tiles in
-// between are kept in a four-entry ring in scalar registers (tl), indexed
-// like the K slots, from which the V loads, the masks and the end test read.
-template <int D, bool BP>
-struct Loop {
-  static constexpr int NS = 4;
-  static constexpr int KT = BN * D;   // elements of one K tile slot
-  static constexpr int VT = D * BN;   // elements of one V^T tile slot
-  static constexpr uint32_t KSLOT = KT * 2, VSLOT = VT * 2;   // bytes
-  static constexpr int DMAS = LoadCtx<D>::PER_K + LoadCtx<D>::PER_V;   // per loading thread
-
-  struct Args {
-    const AttnParams& p;
-    const LoadCtx<D>& lc;
-    uint16_t* lds;
-    int head, rng1, hg;
-    float sl2;
-    const int* kaddr;
-    const int* vaddr;
-    const bf16x8* qf;
+  // A lane's query fragments (d = 16i+8hg..+8 of its query), the LDS element
+  // offsets of its K A-operand reads, and the block-constant K load
+  // addressing of a loading thread.  The K page [H][ps][D] and the V page
+  // [H][D][ps] of one head have the same size.
+  template <int D>
+  struct Ctx {
+    static constexpr int DK = D / 16;   // k-steps of S^T = K Q^T
+    bf16x8 qf[DK];
+    int kaddr[DK];
+    const char* k_head;                 // K pages + head offset (bytes)
+    int64_t page_bytes;
+    uint32_t koff[PER_K<D>];            // per-lane byte offsets of the thread's chunks
   };
 
-  // Step j with J = j mod NS.  Scores of tile j are in s_cur.  Returns false
-  // after the softmax of the last tile (its P V runs after the loop).  On
-  // the last tile the S(j+1) product runs on whatever the K slot holds and
-  // is discarded (cheaper than a branch in the scheduled block).
-  template <int J, bool LAG>
-  static __device__ __forceinline__ bool step(const Args& a, Walk& wk, Tile* tl, int& bad_u,
-                                              int& bad_v, int& last, f32x16* s_cur,
-                                              f32x16* s_nxt, bf16x8* pb, f32x16* o,
-                                              float& m_run, float* l_acc) {
-    const Tile tj = tl[J];   // tile j: its window masks S(j)
-    // the page read issued by the last step lands here, before any LDS read
-    // is in flight: a pending scalar load inside the compute block would
-    // force lgkmcnt(0) at every fragment read
-    asm volatile("" ::"s"(wk.page));
-    const Tile tk = walk_tile<BP>(a.p, a.rng1, wk, bad_u);   // tile j+4
-    walk_next<BP>(a.p, a.rng1, wk);
-    if (!LAG) {
-      load_k<D, BP, J * KSLOT>(a.p, a.lc, a.head, tk, a.lds, bad_v);
-      load_v<D, BP, NS * KSLOT + ((J + 2) % NS) * VSLOT>(a.p, a.lc, a.head, tl[(J + 2) % NS],
-                                                        a.lds, bad_v);
+  template <int D>
+  static __device__ __forceinline__ void setup(const AttnParams& p, const Extra&, int head,
+                                               int qrow, bool qvalid, int wave, int ql, int hg,
+                                               int lq, uint32_t wave_lds, uint16_t* lds,
+                                               Ctx<D>& c) {
+    constexpr int DK = Ctx<D>::DK;
+    const uint16_t* qp = static_cast<const uint16_t*>(p.q) + (int64_t)qrow * p.q_stride +
+                         head * D + 8 * hg;
+#pragma unroll
+    for (int i = 0; i < DK; ++i) {
+      uint4 v = qvalid ? *reinterpret_cast<const uint4*>(qp + 16 * i) : make_uint4(0, 0, 0, 0);
+      c.qf[i] = __builtin_bit_cast(bf16x8, v);
     }
-    tl[J] = tk;
-    if (tile_cut(tj)) {
-      int lo, hi;
-      tile_window(a.p, tj, lo, hi);
-      mask_tile<D>(s_cur, tile_kt(tj), lo, hi, a.hg);
-    }
-    softmax_qk<D>(a.lds + ((J + 1) % NS) * KT, a.kaddr, a.qf, s_cur, s_nxt, m_run, l_acc, a.sl2,
-                  pb);
-    if (tl[(J + 1) % NS].ktc < 0) {
-      last = J;   // P(j) V(j) of the last tile runs after the loop
-      return false;
-    }
-    const uint16_t* vb = a.lds + NS * KT + J * VT;
-    float m_new;
-    if (!LAG && pv_max<D>(vb, a.vaddr, pb, o, s_nxt, m_run, a.sl2, m_new))
-      rescale<D>(o, l_acc, m_run, m_new);
-    // a bare barrier: __syncthreads() would also drain every outstanding
-    // load (its fence waits for vmcnt(0)), emptying the ring each step
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // register-path LDS stores
-    if (!LAG) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(DMAS) : "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    if (LAG && pv_max<D>(vb, a.vaddr, pb, o, s_nxt, m_run, a.sl2, m_new))
-      rescale<D>(o, l_acc, m_run, m_new);
-    return true;
+    const int kr = sigma(ql);
+    const int ku = hg ^ kswz<D>(kr);
+#pragma unroll
+    for (int i = 0; i < DK; ++i) c.kaddr[i] = kr * D + ((2 * i) ^ ku) * 8;
+    const int ps = 1 << p.ps_log2;
+    c.k_head = static_cast<const char*>(p.k_pages) + (int64_t)head * ps * D * 2;
+    c.page_bytes = (int64_t)p.heads * ps * D * 2;
+    // chunk i of a loading thread is row r0 + i*LT/CPR, which has the same
+    // swizzle (a multiple of 16 rows further)
+    constexpr int CPR = D / 8;
+    static_assert((LT / CPR) % 16 == 0, "chunk rows keep their swizzle");
+    const int r0 = lq / CPR, kcol = (lq % CPR) ^ kswz<D>(r0);
+#pragma unroll
+    for (int i = 0; i < PER_K<D>; ++i)
+      c.koff[i] = (uint32_t)((r0 + i * (LT / CPR)) * D + kcol * 8) * 2u;
   }
 
-  template <bool LAG>
-  static __device__ __forceinline__ void run(const Args& a, int rng0, f32x16* o, float& m_run,
-                                             float* l_acc, int& bad_u, int& bad_v) {
-    // prologue: K(0..3), V(0..1), then S(0) and the first running max
-    Walk wk = walk_first<BP>(a.p, rng0);
-    Tile tl[NS];
-#define WF_PRO_K(I)                                                          \
-  tl[I] = walk_tile<BP>(a.p, a.rng1, wk, bad_u);                             \
-  walk_next<BP>(a.p, a.rng1, wk);                                            \
-  if (!LAG) load_k<D, BP, (I) * KSLOT>(a.p, a.lc, a.head, tl[I], a.lds, bad_v);
-    WF_PRO_K(0)
-    WF_PRO_K(1)
-    WF_PRO_K(2)
-    WF_PRO_K(3)
-#undef WF_PRO_K
-    if (!LAG) {
-      load_v<D, BP, NS * KSLOT>(a.p, a.lc, a.head, tl[0], a.lds, bad_v);
-      load_v<D, BP, NS * KSLOT + VSLOT>(a.p, a.lc, a.head, tl[1], a.lds, bad_v);
+  // ---- global -> LDS: the K tile [BN][D] of one head into the slot at byte
+  // KOFF.  A full tile goes by direct loads (PER_K per thread, left in
+  // flight); any other tile takes the register path and ends with every
+  // older vector load complete.
+  template <int D, bool BP, uint32_t KOFF, uint32_t XOFF>
+  static __device__ __forceinline__ void load_k(const AttnParams& p, const Ctx<D>& c,
+                                                uint32_t wave_lds, int head, const Tile& t,
+                                                uint16_t* __restrict__ lds, int& bad) {
+    constexpr int CPR = D / 8;   // chunks per K row
+    constexpr int PER = PER_K<D>;
+    const int ps = 1 << p.ps_log2;
+    if (tile_full(t)) {
+      const char* base = c.k_head + (int64_t)t.page * c.page_bytes +
+                         (int64_t)(tile_kt(t) & (ps - 1)) * (D * 2);
+      dma_chunks<KOFF, 0, PER>(base, c.koff, wave_lds);
+      return;
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    f32x16 sa[Frag<D>::SB], sb[Frag<D>::SB];
-    qk<D>(a.lds, a.kaddr, a.qf, sa);
-    if (tile_cut(tl[0])) {
+    if (t.ktc >= 0) {
+      // rare (tile cut by a range boundary, spread over several pages, or on
+      // a bad page): one chunk at a time, to keep register pressure off the
+      // hot loop.  Rows outside the window hold bf16 quiet NaNs: their scores
+      // are NaN, which the row max skips (IEEE maxNum), and the mask sets
+      // them to -inf before any exponential, so the max of a cut tile is exact.
+      const int tid = threadIdx.x;
+      const uint16_t* __restrict__ kpg = static_cast<const uint16_t*>(p.k_pages);
+      uint16_t* kbuf = lds + KOFF / 2;
+      const uint4 nan8 = make_uint4(0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u);
+      const uint4 zero = make_uint4(0, 0, 0, 0);
       int lo, hi;
-      tile_window(a.p, tl[0], lo, hi);
-      mask_tile<D>(sa, tile_kt(tl[0]), lo, hi, a.hg);
+      tile_window(p, t, lo, hi);
+#pragma unroll 1
+      for (int i = 0; i < PER; ++i) {
+        const int q = i * LT + tid;
+        const int r = q / CPR, col = (q % CPR) ^ kswz<D>(r);
+        const int L = tile_kt(t) + r;
+        uint4 val = nan8;
+        if (L >= lo && L < hi) {
+          const int page = BP ? t.page : lookup_page(p, L, bad);
+          val = zero;
+          if (page >= 0)
+            val = *reinterpret_cast<const uint4*>(
+                kpg + (((int64_t)page * p.heads + head) * ps + (L & (ps - 1))) * D + col * 8);
+        }
+        *reinterpret_cast<uint4*>(kbuf + q * 8) = val;
+      }
     }
-    // finite floor: a row with no visible key in the first tile keeps exact
-    // zero probabilities instead of -inf - -inf
-    m_run = fmaxf(tile_max<D>(sa, a.sl2), -1e30f);
-    // step 0 loads K(4) into the slot of K(0): every wave must have read
-    // K(0) first (write-after-read across waves)
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    bf16x8 pb[Frag<D>::PK];
-    int last = 0;
-    while (true) {
-#define WF_STEP(J, SC, SN)                                                                   \
-  if (!step<J, LAG>(a, wk, tl, bad_u, bad_v, last, SC, SN, pb, o, m_run, l_acc)) break;
-      WF_STEP(0, sa, sb)
-      WF_STEP(1, sb, sa)
-      WF_STEP(2, sa, sb)
-      WF_STEP(3, sb, sa)
-#undef WF_STEP
-    }
-    pv<D>(a.lds + NS * KT + last * VT, a.vaddr, pb, o);
-    // no LDS-DMA may still be in flight when the block ends
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+
+  // S^T of one tile: s[sb] for keys 32sb.. of the K slot at byte KOFF
+  template <int D, uint32_t KOFF, uint32_t XOFF>
+  static __device__ __forceinline__ void qk(const uint16_t* __restrict__ lds, const Ctx<D>& c,
+                                            f32x16* s) {
+    const uint16_t* kbuf = lds + KOFF / 2;
+#pragma unroll
+    for (int sb = 0; sb < Frag<D>::SB; ++sb) {
+      s[sb] = f32x16{};
+#pragma unroll
+      for (int i = 0; i < Ctx<D>::DK; ++i) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kbuf + c.kaddr[i] + 32 * sb * D);
+        s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, c.qf[i], s[sb], 0, 0, 0);
+      }
+    }
+  }
+
+  // Instruction-scheduling hint for the block that issues the S(j+1) MFMAs
+  // and the softmax of tile j: K reads run a few ahead, and every MFMA is
+  // followed by a share of the vector work (the tile's 32 exponentials and
+  // about 64 other instructions over 16 MFMAs), so the matrix pipe and the
+  // VALU run together.  The grouping counts the exponential as a
+  // transcendental (mask 0x400), not as a plain vector instruction (0x002):
+  // a group that names only the latter leaves the exponentials to bunch
+  // behind the first MFMAs.  Three of each per MFMA (the exponentials done by
+  // the eleventh MFMA, the rest of the vector work trailing) measured 3 %
+  // faster than an even two and four.
+  template <int D>
+  static __device__ __forceinline__ void interleave_qk_softmax() {
+    constexpr int NM = Frag<D>::SB * Ctx<D>::DK;   // MFMAs of S(j+1)
+    constexpr int AHEAD = 3;
+    constexpr int TPM = 3;                          // exponentials per MFMA
+    constexpr int VPM = 3;                          // other VALU per MFMA
+#pragma unroll
+    for (int k = 0; k < AHEAD; ++k) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+    for (int k = 0; k < NM; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x400, TPM, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);
+      if (k + AHEAD < NM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
   }
 };
 
 template <int D, bool BP>
 __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_bf16(const AttnParams p) {
-  using L = Loop<D, BP>;
-  constexpr int DK = Frag<D>::DK, DB = Frag<D>::DB, PK = Frag<D>::PK;
-  constexpr int NS = L::NS, KT = L::KT, VT = L::VT;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[NS * (KT + VT)];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int ql = lane & 31, hg = lane >> 5;
-
-  // ---- work item: XCD-contiguous runs, longest first within each --------
-  const int w = xcd_work_item(p, blockIdx.x, gridDim.x);
-  const int head = w / p.tiles_per_head;
-  const int tw = w - head * p.tiles_per_head;
-  int grp = 0;
-  while (tw >= p.grp_tile_end[grp]) ++grp;
-  const int qtile = tw - (grp ? p.grp_tile_end[grp - 1] : 0);
-  const int row_end = p.grp_row1[grp];
-  const int qrow = p.grp_row0[grp] + qtile * BM + wave * 32 + ql;
-  const bool qvalid = qrow < row_end;
-  const int rng0 = p.grp_rng0[grp], rng1 = p.grp_rng1[grp];
-
-  // lane (query ql, half hg) holds d = 16i+8hg..+8 of its query
-  bf16x8 qf[DK];
-  {
-    const uint16_t* qp = static_cast<const uint16_t*>(p.q) + (int64_t)qrow * p.q_stride +
-                         head * D + 8 * hg;
-#pragma unroll
-    for (int i = 0; i < DK; ++i) {
-      uint4 v = qvalid ? *reinterpret_cast<const uint4*>(qp + 16 * i) : make_uint4(0, 0, 0, 0);
-      qf[i] = __builtin_bit_cast(bf16x8, v);
-    }
-  }
-  // per-lane LDS element offsets of the A-operand reads
-  int kaddr[DK], vaddr[PK];
-  {
-    const int kr = sigma(ql);
-    const int ku = hg ^ kswz<D>(kr);
-#pragma unroll
-    for (int i = 0; i < DK; ++i) kaddr[i] = kr * D + ((2 * i) ^ ku) * 8;
-    const int vu = hg ^ vswz(ql);
-#pragma unroll
-    for (int t = 0; t < PK; ++t) vaddr[t] = ql * BN + ((2 * t) ^ vu) * 8;
-  }
-
-  // block-constant load addressing
-  LoadCtx<D> lc;
-  {
-    const int ps = 1 << p.ps_log2;
-    const int64_t head_bytes = (int64_t)head * ps * D * 2;
-    lc.k_head = static_cast<const char*>(p.k_pages) + head_bytes;
-    lc.v_head = static_cast<const char*>(p.v_pages) + head_bytes;
-    lc.page_bytes = (int64_t)p.heads * ps * D * 2;
-    // K: chunk i of a loading thread is row r0 + i*LT/CPR, which has the
-    // same swizzle (a multiple of 16 rows further); V: feature row
-    // d0 + i*LT/8 (also a multiple of 16 further)
-    constexpr int CPR = D / 8;
-    static_assert((LT / CPR) % 16 == 0 && (LT / 8) % 16 == 0, "chunk rows keep their swizzle");
-    const int q = (wave % (LT / 64)) * 64 + lane;
-    const int r0 = q / CPR, kcol = (q % CPR) ^ kswz<D>(r0);
-#pragma unroll
-    for (int i = 0; i < LoadCtx<D>::PER_K; ++i)
-      lc.koff[i] = (uint32_t)((r0 + i * (LT / CPR)) * D + kcol * 8) * 2u;
-    const int d0 = q >> 3, vcol = (q & 7) ^ vswz(d0);
-#pragma unroll
-    for (int i = 0; i < LoadCtx<D>::PER_V; ++i)
-      lc.voff[i] = (uint32_t)((d0 + i * (LT / 8)) * ps + vcol * 8) * 2u;
-    lc.wave_lds = (uint32_t)(uintptr_t)lds + (uint32_t)__builtin_amdgcn_readfirstlane(wave) * 1024u;
-  }
-
-  f32x16 o[DB];
-#pragma unroll
-  for (int i = 0; i < DB; ++i) o[i] = f32x16{};
-  float m_run;               // running max of scale*log2(e)*<q,k>
-  float l_acc[2] = {0.f, 0.f};
-  int bad_u = 0, bad_v = 0;  // bad page entries: wave-uniform and per-lane
-  const typename L::Args args{p, lc, lds, head, rng1, hg, p.scale_log2, kaddr, vaddr, qf};
-  // waves NW/2.. run half a tile behind (see Loop)
-  if (wave >= NW / 2)
-    L::template run<true>(args, rng0, o, m_run, l_acc, bad_u, bad_v);
-  else
-    L::template run<false>(args, rng0, o, m_run, l_acc, bad_u, bad_v);
-  // one status write per wave that met a bad page entry (per-lane lookups
-  // of the register path included)
-  if ((bad_u | (__builtin_amdgcn_ballot_w64(bad_v != 0) != 0)) && lane == 0)
-    atomicOr(p.status, WF_STATUS_BAD_PAGE);
-
-  // ---- epilogue: O = O^T / l, LSE ------------------------------------------
-  const float l = xhalf_sum(l_acc[0] + l_acc[1]);
-  const float inv = 1.0f / l;
-  if (qvalid) {
-    uint16_t* op = static_cast<uint16_t*>(p.out) + (int64_t)qrow * p.out_stride + head * D;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        // registers 4j..4j+3 of block db: d = 32db + 8j + 4hg + 0..3
-        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-        bf16x4 v;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = (__bf16)(o[db][4 * j + e] * inv);
-        *reinterpret_cast<bf16x4*>(op + 32 * db + 8 * j + 4 * hg) = v;
-      }
-    if (p.lse && hg == 0)
-      p.lse[(int64_t)head * p.lse_stride + qrow] = (m_run + __log2f(l)) * kLn2;
-  }
+  __shared__ __attribute__((aligned(16))) uint16_t lds[Loop<ScoreBf16, D, BP>::LDS_BYTES / 2];
+  attn_body<ScoreBf16, D, BP>(p, ScoreBf16::Extra{}, lds);
 }
 
 }  // namespace

@@ -29,35 +29,13 @@
 #include "../../include/wf.h"
 #include "wf_internal.h"
 #include "wf_mx.h"
+#include "wf_numerics.h"
 
 namespace wf {
 namespace {
 
 constexpr int kTileTok = 64;
 constexpr int kThreads = 256;
-
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
-
-__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
-  return __uint_as_float((uint32_t)b << 16);
-}
-
-// rotate one pair: y0 = x0*c - x1*s, y1 = x0*s + x1*c, every operation
-// rounded on its own
-__device__ __forceinline__ void rotate(float x0, float x1, float2 cs, float& y0, float& y1) {
-#pragma clang fp contract(off)
-  const float a = x0 * cs.x;
-  const float b = x1 * cs.y;
-  const float c = x0 * cs.y;
-  const float d = x1 * cs.x;
-  y0 = a - b;
-  y1 = c + d;
-}
 
 // rotate the pairs of one 16-byte vector in place (storage type T)
 template <typename T>
@@ -68,43 +46,15 @@ __device__ __forceinline__ void rotate_vec(uint4& v, const float2* cs) {
   for (int j = 0; j < EPV / 2; ++j) {
     float y0, y1;
     if constexpr (sizeof(T) == 2) {
-      rotate(bf16_to_f32(e[2 * j]), bf16_to_f32(e[2 * j + 1]), cs[j], y0, y1);
+      rotate_pair(bf16_to_f32(e[2 * j]), bf16_to_f32(e[2 * j + 1]), cs[j], y0, y1);
       e[2 * j] = f32_to_bf16_rne(y0);
       e[2 * j + 1] = f32_to_bf16_rne(y1);
     } else {
-      rotate(e[2 * j], e[2 * j + 1], cs[j], y0, y1);
+      rotate_pair(e[2 * j], e[2 * j + 1], cs[j], y0, y1);
       e[2 * j] = y0;
       e[2 * j + 1] = y1;
     }
   }
-}
-
-// ---- MXFP8 keys (OCP microscaling: E4M3 codes, one E8M0 scale per 32
-// features) --------------------------------------------------------------
-// Shared scale code of a block whose largest magnitude is amax:
-// floor(log2 amax) - 8 + 127 clamped at 0, i.e. the float exponent field of
-// amax minus 8 (0 for zero and for amax below 2^-119).
-__device__ __forceinline__ uint32_t mx_scale_code(float amax) {
-  const int e = (int)((__float_as_uint(amax) >> 23) & 0xffu) - 8;
-  return (uint32_t)max(e, 0);
-}
-
-// E4M3 code of y (finite), nearest value with ties to even, saturating at
-// +-448; the sign of zero is kept.
-__device__ __forceinline__ uint32_t e4m3_code(float y) {
-  const uint32_t s = (__float_as_uint(y) >> 24) & 0x80u;
-  const float a = fminf(fabsf(y), 448.0f);
-  uint32_t c;
-  if (a < 0.015625f) {
-    c = (uint32_t)__builtin_rintf(a * 512.0f);   // subnormal grid, step 2^-9
-  } else {
-    // keep 3 of the 23 mantissa bits, rounding to nearest even; a carry
-    // moves into the exponent; rebias 127 -> 7
-    uint32_t b = __float_as_uint(a);
-    b += 0x7ffffu + ((b >> 20) & 1u);
-    c = (b >> 20) - (120u << 3);
-  }
-  return s | c;
 }
 
 // Streaming 16-byte loads and stores: every input byte is read once and every
@@ -229,10 +179,7 @@ __device__ __forceinline__ void k_block(
         const int L = T0 + ti;
         if (L < lo || L >= hi) continue;
         const int t = L - p.dst_start;
-        const double phi = (double)p.pos[(int64_t)t * 3 + p.pair_axis[pr]] * p.pair_omega[pr];
-        double sn, cn;
-        sincos(phi, &sn, &cn);
-        sm.cs[ti][pr] = make_float2((float)cn, (float)sn);
+        sm.cs[ti][pr] = rotary_factors(p.pos[(int64_t)t * 3 + p.pair_axis[pr]], p.pair_omega[pr]);
       }
     }
     __syncthreads();   // factors (and, in the first pass, page_of) visible
