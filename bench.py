@@ -105,7 +105,7 @@ def traffic_from_profiles(kernel_src_hash: str):
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for name in ("attn_bf16.hip", "wf_internal.h"):
+    for name in ("attn_bf16.hip", "attn_core.h", "wf_internal.h"):
         with open(os.path.join(ROOT, "chunk_wise_causal_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
