@@ -415,18 +415,21 @@ __device__ __forceinline__ void rescale(f32x16* o, float* l_acc, float& m_run, f
 // P(j) V(j) while a lagging wave runs P(j-1) V(j-1) then softmax(j); the two
 // waves sharing a SIMD are one of each group, so while one issues the
 // softmax's vector work the other keeps the matrix pipe busy.
-// At tile j the slots hold K(j+1..j+4) and V(j-1..j+2); step j issues
-// K(j+4) into the slot of K(j) and V(j+2) into the slot of V(j-2), both read
-// by every wave before the previous barrier.  Only the leading waves issue
-// loads: they finish their half-tiles early and would otherwise idle at the
-// barrier, while the lagging waves' softmax is the critical path.  The
-// barrier of step j must publish K(j+2) and V(j+1), issued in earlier steps:
-// each loading wave waits until no more than this step's direct loads are
-// outstanding (vector loads complete in order), then the barrier publishes
-// them to all waves.
-// The walk runs once per step, four tiles ahead (for K); the tiles in
-// between are kept in a four-entry ring in scalar registers (tl), indexed
-// like the K slots, from which the V loads, the masks and the end test read.
+// Step j starts by issuing K(j+3) into the slot of K(j-1) and V(j+2) into
+// the slot of V(j-2), both read by every wave before the previous barrier.
+// Only the leading waves issue loads: they finish their half-tiles early and
+// would otherwise idle at the barrier, while the lagging waves' softmax is
+// the critical path.  The barrier of step j must publish K(j+2) and V(j+1),
+// issued in earlier steps: each loading wave waits until no more than this
+// step's direct loads are outstanding (vector loads complete in order), then
+// the barrier publishes them to all waves.
+// The walk runs once per step and yields tile j+4; the tiles in between are
+// kept in a four-entry ring in scalar registers (tl), indexed like the K
+// slots, from which the loads, the masks and the end test read.  A leading
+// wave walks after its P V block, a lagging wave at the step start (after
+// its own P V): either way the walk's scalar work stays out of the softmax
+// block that bounds the step (walking at the step start in the leading
+// waves measured 1-2 % slower).
 //
 // LDS layout: NS K slots of S::KSLOT<D> bytes, NS V^T slots, NS extra slots
 // of S::XSLOT<D> bytes.
@@ -492,15 +495,16 @@ struct Loop {
     // is in flight: a pending scalar load inside the compute block would
     // force lgkmcnt(0) at every fragment read
     asm volatile("" ::"s"(wk.page));
-    const Tile tk = walk_tile<BP>(a.p, a.rng1, wk, bad_u);   // tile j+4
-    walk_next<BP>(a.p, a.rng1, wk);
+    constexpr int JK = (J + 3) % NS;   // the slot of K(j-1) and K(j+3)
     if (!LAG) {
-      S::template load_k<D, BP, J * KSLOT, XBASE + J * XSLOT>(a.p, a.kc, a.lc.wave_lds, a.head,
-                                                               tk, a.lds, bad_v);
+      S::template load_k<D, BP, JK * KSLOT, XBASE + JK * XSLOT>(a.p, a.kc, a.lc.wave_lds, a.head,
+                                                                 tl[JK], a.lds, bad_v);
       load_v<D, BP, VBASE + ((J + 2) % NS) * VSLOT>(a.p, a.lc, a.head, tl[(J + 2) % NS], a.lds,
                                                     bad_v);
+    } else {
+      tl[J] = walk_tile<BP>(a.p, a.rng1, wk, bad_u);   // tile j+4
+      walk_next<BP>(a.p, a.rng1, wk);
     }
-    tl[J] = tk;
     if (tile_cut(tj)) {
       int lo, hi;
       tile_window(a.p, tj, lo, hi);
@@ -513,8 +517,12 @@ struct Loop {
     }
     const uint16_t* vb = vslot(a.lds, J);
     float m_new;
-    if (!LAG && pv_max<D>(vb, a.vaddr, pb, o, s_nxt, m_run, a.sl2, m_new))
-      rescale<D>(o, l_acc, m_run, m_new);
+    if (!LAG) {
+      if (pv_max<D>(vb, a.vaddr, pb, o, s_nxt, m_run, a.sl2, m_new))
+        rescale<D>(o, l_acc, m_run, m_new);
+      tl[J] = walk_tile<BP>(a.p, a.rng1, wk, bad_u);   // tile j+4
+      walk_next<BP>(a.p, a.rng1, wk);
+    }
     // a bare barrier: __syncthreads() would also drain every outstanding
     // load (its fence waits for vmcnt(0)), emptying the ring each step
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // register-path LDS stores
@@ -529,13 +537,14 @@ struct Loop {
   template <bool LAG>
   static __device__ __forceinline__ void run(const Args& a, int rng0, f32x16* o, float& m_run,
                                              float* l_acc, int& bad_u, int& bad_v) {
-    // prologue: K(0..3), V(0..1), then S(0) and the first running max
+    // prologue: the walk's first four tiles, K(0..2), V(0..1), then S(0)
+    // and the first running max (step 0 loads K(3))
     Walk wk = walk_first<BP>(a.p, rng0);
     Tile tl[NS];
 #define WF_PRO_K(I)                                                                   \
   tl[I] = walk_tile<BP>(a.p, a.rng1, wk, bad_u);                                      \
   walk_next<BP>(a.p, a.rng1, wk);                                                     \
-  if (!LAG)                                                                           \
+  if (!LAG && (I) < NS - 1)                                                           \
     S::template load_k<D, BP, (I) * KSLOT, XBASE + (I) * XSLOT>(a.p, a.kc, a.lc.wave_lds, \
                                                                  a.head, tl[I], a.lds, bad_v);
     WF_PRO_K(0)
@@ -559,8 +568,8 @@ struct Loop {
     // finite floor: a row with no visible key in the first tile keeps exact
     // zero probabilities instead of -inf - -inf
     m_run = fmaxf(tile_max<D>(sa, a.sl2), -1e30f);
-    // step 0 loads K(4) into the slot of K(0): every wave must have read
-    // K(0) first (write-after-read across waves)
+    // both wave groups enter the loop together (the lagging group falls
+    // half a tile behind at its first barrier)
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
