@@ -293,7 +293,10 @@ int publish_impl(const wf_kv_pool* pool, const wf_mx_keys* mx, const wf_rope* ro
   // block), V blocks 256 features (bfloat16) or one head (float32)
   const int64_t tiles = ((int64_t)dst_logical_start + n_tok - 1) / 64 - dst_logical_start / 64 + 1;
   p.tiles = (int)tiles;
-  const int kgroups = (pool->num_heads + 9) / 10;
+  // K blocks per tile: heads split into at most four groups of at least
+  // four (measured: 4 groups of 10 at 40 heads, 3 groups of 4 at 12 heads;
+  // more, smaller groups repeat the rotary factors, fewer leave a tail)
+  const int kgroups = std::min(4, (pool->num_heads + 3) / 4);
   p.heads_per_kblock = (pool->num_heads + kgroups - 1) / kgroups;
   const int64_t v_per_tile = (mx || pool->dtype == WF_BF16)
                                  ? (pool->num_heads * pool->head_dim / 64 + 3) / 4
