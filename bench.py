@@ -325,6 +325,29 @@ def time_publish_flushed(cfg, torch, wf, pool, k_t, v_t, pos_t, steps: int):
             "flush": "512 MB device buffer overwritten before each launch"}
 
 
+def copy_ceiling(torch, nbytes: int, steps: int):
+    """A measured HBM ceiling beside the spec peak: a plain device copy
+    (torch copy_) that reads and writes the publish's byte count (half read,
+    half written), HIP events around each copy, median."""
+    n = nbytes // 4
+    a = torch.empty(n, dtype=torch.bfloat16, device="cuda").normal_()
+    b = torch.empty_like(a)
+    stream = torch.cuda.current_stream()
+    ms = []
+    for i in range(steps + 3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        b.copy_(a)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if i >= 3:
+            ms.append(e0.elapsed_time(e1))
+    del a, b
+    torch.cuda.empty_cache()
+    med = float(np.median(ms))
+    return round(4 * n / (med * 1e-3) / 1e9, 1)
+
+
 def time_layer_tick(cfg, torch, wf, steps: int, warmup: int):
     """One layer tick of another configuration, timed like the headline:
     the round's publish then the attention on one stream, HIP events around
@@ -491,6 +514,11 @@ def main():
     }
     res["publish_flushed"] = time_publish_flushed(cfg, torch, wf, pool, k_t, v_t, pos_t,
                                                   args.steps)
+    copy_gbps = copy_ceiling(torch, pub_bytes, args.steps)
+    res["measured_ceilings"] = {
+        "copy_GBps": copy_gbps, "copy_frac_hbm_peak": round(copy_gbps / PEAK_HBM_GBPS, 4),
+        "publish_over_copy": round(pub_gbps / copy_gbps, 4),
+        "copy": "device copy (torch copy_) reading and writing the publish's byte count"}
     res["history_rotate"] = time_history_rotate(cfg, torch, wf)
     res["mx_variant"] = time_mx_variant(cfg, torch, wf, q, k, v, pos, pool, out, args.steps)
     res["qkv_publish"] = time_qkv_publish(cfg, torch, wf, pos, args.steps)
