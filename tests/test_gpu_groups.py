@@ -119,3 +119,40 @@ def test_store_stage_alone_on_offset_rows():
     assert np.isnan(got[:r0]).all() and np.isnan(got[r1:]).all()
     mx, rr = G.err_stats(got[r0:r1], o_ref[r0:r1])
     assert mx <= G.MAX_ABS and rr <= G.REL_RMS
+
+
+@pytest.mark.parametrize("cuts", [(1000,), (333, 1347), (64, 65, 1900)], ids=["2", "3", "4"])
+def test_lse_merge_of_key_partitions(cuts):
+    """Attention of all query rows over disjoint key ranges (unaligned cuts,
+    one range a single key), merged on the host by e^LSE, against the
+    oracle over the union: the LSE the kernel reports is the normalizer of
+    the O it returns, so partial results combine (as a split of the keys
+    across calls or devices would) within the single call's tolerances."""
+    cfg = medium(page_size=64, seed=31)
+    assert cuts[-1] < cfg.n_kv
+    wl = make_workload(cfg)
+    ref = oracle_layer(wl)
+    pool, q, _ = G.gpu_layer(wl)
+    c = wl.cfg
+    print(f"\n[case] key partition at {cuts}: {cfg}", flush=True)
+    edges = [0, *cuts, c.n_kv]
+    outs, lses = [], []
+    for a, b in zip(edges[:-1], edges[1:]):
+        out = torch.full_like(q, float("nan"))
+        lse = torch.full((c.heads, c.n_q), float("nan"), device=G.DEV)
+        wf.wf_group_attn(pool, [(a, b - a)], [(0, c.n_q, 0, 1)], q, c.scale, out=out, lse=lse)
+        outs.append(G.to_f64(out))
+        lses.append(G.to_f64(lse))
+    torch.cuda.synchronize()
+    lse = np.stack(lses)                              # [P, H, n]
+    top = lse.max(axis=0)
+    w = np.exp(lse - top)
+    den = w.sum(axis=0)
+    merged = sum(w[i].T[:, :, None] * outs[i] for i in range(len(outs))) / den.T[:, :, None]
+    o_ref, l_ref = group_attention(ref["k_pool"], ref["v_pool"], wl.page_table, c.page_size,
+                                   [(0, c.n_kv)], [(0, c.n_q, 0, 1)], ref["q"], c.scale, c.dtype)
+    mx, rr = G.err_stats(merged, o_ref)
+    dl = np.abs(top + np.log(den) - l_ref).max()
+    print(f"merged: max-abs {mx:.3e} rel-rms {rr:.3e} lse {dl:.3e}", flush=True)
+    assert mx <= G.MAX_ABS and rr <= G.REL_RMS
+    assert dl <= G.lse_atol(c.dtype)

@@ -273,3 +273,31 @@ def test_slot_rule_as_groups_reproduces_chunk_attention():
 
 def test_run_tokens_is_the_union():
     assert list(run_tokens([(5, 2), (0, 3)])) == [0, 1, 2, 5, 6]
+
+
+def _merge(parts):
+    """Merge (out, lse) results over disjoint key sets by their natural-log
+    LSE: weights e^lse, shifted by the row maximum."""
+    lse = np.stack([p[1] for p in parts])            # [P, H, n]
+    top = np.max(lse, axis=0)
+    w = np.exp(lse - top)                            # [P, H, n]
+    den = w.sum(axis=0)
+    num = sum(w[i].T[:, :, None] * parts[i][0] for i in range(len(parts)))
+    return num / den.T[:, :, None], top + np.log(den)
+
+
+@pytest.mark.parametrize("cuts", [(1,), (37, 200), (64, 65, 201)], ids=["1", "2", "3"])
+def test_lse_merges_key_partitions(cuts):
+    """The LSE is the natural-log normalizer: attention over disjoint key
+    sets, merged by e^LSE, gives attention over their union (an LSE in log2
+    units or one that leaves out the scale fails this)."""
+    wl = make_workload(small_config(slots=2, seed=5))
+    ref = oracle_layer(wl)
+    c = wl.cfg
+    rows = (0, c.n_q)
+    full = _gattn(wl, ref, [(0, c.n_kv)], [(*rows, 0, 1)])
+    edges = [0, *cuts, c.n_kv]
+    parts = [_gattn(wl, ref, [(a, b - a)], [(*rows, 0, 1)]) for a, b in zip(edges[:-1], edges[1:])]
+    out, lse = _merge(parts)
+    np.testing.assert_allclose(out, full[0], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, full[1], rtol=0, atol=1e-12)
