@@ -58,8 +58,12 @@ constexpr int A_BYTES = BM * ROWB;         // 16 KB of W rows per tile
 constexpr int B_BYTES = BN * ROWB;         // 16 KB of x rows per tile
 constexpr int SLOT = A_BYTES + B_BYTES;    // 32 KB
 constexpr int RING = NSL * SLOT;           // 128 KB
-constexpr int A_DMA = A_BYTES / (NTH * 16);  // 16-byte loads per thread per tile: 2
-constexpr int B_DMA = B_BYTES / (NTH * 16);  // 2
+#ifndef WF_QKV_LW
+#define WF_QKV_LW 4
+#endif
+constexpr int LW = WF_QKV_LW;                 // waves that issue the tile loads (one per SIMD)
+constexpr int A_DMA = A_BYTES / (LW * 64 * 16);  // 16-byte loads per loading thread per tile: 4
+constexpr int B_DMA = B_BYTES / (LW * 64 * 16);  // 4
 constexpr int DMAS = A_DMA + B_DMA;
 constexpr int NPAIR = D / 2;
 // past the ring: the positions of the block's tokens (int4 per token), the
@@ -71,7 +75,8 @@ constexpr int RB_OFF = HDR_OFF + 32 * 4;       // int[NPAIR]
 constexpr int TAB_OFF = RB_OFF + NPAIR * 4;
 constexpr int LDS_BYTES = 160 * 1024;
 constexpr int TAB_CAP = (LDS_BYTES - TAB_OFF) / 8;
-static_assert(A_DMA == 2 && B_DMA == 2, "two loads of each operand per thread and tile");
+static_assert(A_DMA * LW * 1024 == A_BYTES && B_DMA * LW * 1024 == B_BYTES && 16 % DMAS == 0,
+              "whole 1 KB runs per loading wave; loads spread evenly over a tile's 16 products");
 static_assert(2 * 64 * D * 2 <= RING && 2 * D * BN * 2 <= RING, "staging fits in the ring");
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -143,15 +148,33 @@ __device__ __forceinline__ int axis_of(const QkvParams& p, int pr) {
 // of the slot).  Tiles past the last one re-load the last tile into a slot
 // no step reads again, so every step issues the same loads and the wait
 // counts are constants.
+// load n of a loading thread's DMAS per tile: W rows first, then x rows;
+// instruction u of loading wave lw fills the 1 KB run LW u + lw of its
+// operand
+template <int N>
+__device__ __forceinline__ void dma_n(const char* wbase, const char* xbase, int kb,
+                                      const uint32_t* aoff, const uint32_t* boff, uint32_t dst) {
+  if constexpr (N < A_DMA)
+    dma16<N * LW * 1024>(wbase + kb, aoff[N], dst);
+  else
+    dma16<A_BYTES + (N - A_DMA) * LW * 1024>(xbase + kb, boff[N - A_DMA], dst);
+}
+
+template <int N = 0>
+__device__ __forceinline__ void dma_all(const char* wbase, const char* xbase, int kb,
+                                        const uint32_t* aoff, const uint32_t* boff, uint32_t dst) {
+  if constexpr (N < DMAS) {
+    dma_n<N>(wbase, xbase, kb, aoff, boff, dst);
+    dma_all<N + 1>(wbase, xbase, kb, aoff, boff, dst);
+  }
+}
+
 __device__ __forceinline__ void load_tile_at(const char* wbase, const char* xbase, int m,
                                              int ktiles, const uint32_t* aoff,
                                              const uint32_t* boff, uint32_t wave_lds) {
   const int kb = min(m, ktiles - 1) * TK * 2;
   const uint32_t dst = wave_lds + (uint32_t)(m % NSL) * SLOT;
-  dma16<0>(wbase + kb, aoff[0], dst);
-  dma16<8192>(wbase + kb, aoff[1], dst);
-  dma16<A_BYTES>(xbase + kb, boff[0], dst);
-  dma16<A_BYTES + 8192>(xbase + kb, boff[1], dst);
+  dma_all(wbase, xbase, kb, aoff, boff, dst);
 }
 
 // the 16 products of the tile whose fragments are in `cur`
@@ -163,11 +186,30 @@ __device__ __forceinline__ void mma_all(const Frags& cur, f32x16 (&acc)[4][2]) {
 }
 
 // Step kt < ktiles - 1 of the k-loop (B = kt % 2: fragment buffer B holds
-// tile kt, the other one receives tile kt+1).  Tile kt+1 is done for this
-// thread when only the loads of tiles kt+2 and kt+3 are in flight, and this
-// wave's reads of tile kt are done; after the barrier tile kt+1 is visible
-// and tile kt's slot is free for tile kt+4.
-template <int B>
+// tile kt, the other one receives tile kt+1).  Tile kt+1 is done for a
+// loading thread when only the loads of tiles kt+2 and kt+3 are in flight,
+// and this wave's reads of tile kt are done; after the barrier tile kt+1 is
+// visible and tile kt's slot is free for tile kt+4.  Only the loading waves
+// (LD, one per SIMD) issue loads: a direct-to-LDS load holds its wave at
+// issue, and the other wave of the SIMD keeps the matrix pipe fed meanwhile.
+// The loads go one every 16 / DMAS products, so that the CU's load path sees
+// an even stream instead of a burst after the barrier; the 12 fragment reads
+// of tile kt+1 go in between the first products.
+template <bool LD, int M>
+__device__ __forceinline__ void after_mma(const char* wbase, const char* xbase, int kb,
+                                          const uint32_t* aoff, const uint32_t* boff,
+                                          uint32_t dst, Frags& nxt, const char* nslot, int ra,
+                                          int rb, const int* xo) {
+  constexpr int EVERY = 16 / DMAS;
+  if constexpr (LD && M % EVERY == 0) dma_n<M / EVERY>(wbase, xbase, kb, aoff, boff, dst);
+  constexpr int R = M < 3 ? 2 * M : (M >= 4 && M < 7 ? 2 * (M - 1) : -1);   // reads 0..11
+  if constexpr (R >= 0) {
+    read_frag<R>(nxt, nslot, ra, rb, xo);
+    read_frag<R + 1>(nxt, nslot, ra, rb, xo);
+  }
+}
+
+template <int B, bool LD>
 __device__ __forceinline__ void k_step(int kt, int ktiles, const char* lds, const char* wbase,
                                        const char* xbase, const uint32_t* aoff,
                                        const uint32_t* boff, uint32_t wave_lds, int ra, int rb,
@@ -180,61 +222,50 @@ __device__ __forceinline__ void k_step(int kt, int ktiles, const char* lds, cons
   const char* nslot = lds + ((kt + 1) % NSL) * SLOT;
   const int kb = min(kt + NSL, ktiles - 1) * TK * 2;
   const uint32_t dst = wave_lds + (uint32_t)(kt % NSL) * SLOT;
-  // one load every 4 products, so that the CU's load path (about 64 bytes
-  // per clock, shared by the 8 waves) sees an even stream instead of a burst
-  // after the barrier; the 12 fragment reads of tile kt+1 go in between
-  fence();
-  mma<0>(cur, acc);
-  fence();
-  dma16<0>(wbase + kb, aoff[0], dst);
-  read_frag<0>(nxt, nslot, ra, rb, xo);
-  read_frag<1>(nxt, nslot, ra, rb, xo);
-  fence();
-  mma<1>(cur, acc);
-  fence();
-  read_frag<2>(nxt, nslot, ra, rb, xo);
-  read_frag<3>(nxt, nslot, ra, rb, xo);
-  fence();
-  mma<2>(cur, acc);
-  fence();
-  read_frag<4>(nxt, nslot, ra, rb, xo);
-  read_frag<5>(nxt, nslot, ra, rb, xo);
-  fence();
-  mma<3>(cur, acc);
-  fence();
-  mma<4>(cur, acc);
-  fence();
-  dma16<8192>(wbase + kb, aoff[1], dst);
-  read_frag<6>(nxt, nslot, ra, rb, xo);
-  read_frag<7>(nxt, nslot, ra, rb, xo);
-  fence();
-  mma<5>(cur, acc);
-  fence();
-  read_frag<8>(nxt, nslot, ra, rb, xo);
-  read_frag<9>(nxt, nslot, ra, rb, xo);
-  fence();
-  mma<6>(cur, acc);
-  fence();
-  read_frag<10>(nxt, nslot, ra, rb, xo);
-  read_frag<11>(nxt, nslot, ra, rb, xo);
-  fence();
-  mma<7>(cur, acc);
-  fence();
-  mma<8>(cur, acc);
-  fence();
-  dma16<A_BYTES>(xbase + kb, boff[0], dst);
-  fence();
-  mma<9>(cur, acc);
-  mma<10>(cur, acc);
-  mma<11>(cur, acc);
-  fence();
-  mma<12>(cur, acc);
-  fence();
-  dma16<A_BYTES + 8192>(xbase + kb, boff[1], dst);
-  fence();
-  mma<13>(cur, acc);
-  mma<14>(cur, acc);
-  mma<15>(cur, acc);
+#define WF_QKV_MMA(M)                                                                 \
+  fence();                                                                            \
+  mma<M>(cur, acc);                                                                   \
+  fence();                                                                            \
+  after_mma<LD, M>(wbase, xbase, kb, aoff, boff, dst, nxt, nslot, ra, rb, xo);
+  WF_QKV_MMA(0) WF_QKV_MMA(1) WF_QKV_MMA(2) WF_QKV_MMA(3)
+  WF_QKV_MMA(4) WF_QKV_MMA(5) WF_QKV_MMA(6) WF_QKV_MMA(7)
+  WF_QKV_MMA(8) WF_QKV_MMA(9) WF_QKV_MMA(10) WF_QKV_MMA(11)
+  WF_QKV_MMA(12) WF_QKV_MMA(13) WF_QKV_MMA(14) WF_QKV_MMA(15)
+#undef WF_QKV_MMA
+}
+
+// The k-loop from the barrier that publishes tile 0 to the products of the
+// last tile: steps 0 .. ktiles-2 (tile m's fragments in buffer m % 2), then
+// the products of the last tile; ktiles = hidden / 32 is even.
+template <bool LD>
+__device__ __forceinline__ void k_loop(int ktiles, const char* lds, const char* wbase,
+                                       const char* xbase, const uint32_t* aoff,
+                                       const uint32_t* boff, uint32_t wave_lds, int ra, int rb,
+                                       const int* xo, f32x16 (&acc)[4][2]) {
+  Frags fr[2];
+  // tile 0: visible after the loading threads' loads of it are done and the barrier
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * DMAS) : "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  if constexpr (LD) load_tile_at(wbase, xbase, NSL - 1, ktiles, aoff, boff, wave_lds);
+  read_frag<0>(fr[0], lds, ra, rb, xo);
+  read_frag<1>(fr[0], lds, ra, rb, xo);
+  read_frag<2>(fr[0], lds, ra, rb, xo);
+  read_frag<3>(fr[0], lds, ra, rb, xo);
+  read_frag<4>(fr[0], lds, ra, rb, xo);
+  read_frag<5>(fr[0], lds, ra, rb, xo);
+  read_frag<6>(fr[0], lds, ra, rb, xo);
+  read_frag<7>(fr[0], lds, ra, rb, xo);
+  read_frag<8>(fr[0], lds, ra, rb, xo);
+  read_frag<9>(fr[0], lds, ra, rb, xo);
+  read_frag<10>(fr[0], lds, ra, rb, xo);
+  read_frag<11>(fr[0], lds, ra, rb, xo);
+  for (int kt = 0; kt < ktiles - 2; kt += 2) {
+    k_step<0, LD>(kt, ktiles, lds, wbase, xbase, aoff, boff, wave_lds, ra, rb, xo, fr, acc);
+    k_step<1, LD>(kt + 1, ktiles, lds, wbase, xbase, aoff, boff, wave_lds, ra, rb, xo, fr, acc);
+  }
+  k_step<0, LD>(ktiles - 2, ktiles, lds, wbase, xbase, aoff, boff, wave_lds, ra, rb, xo, fr, acc);
+  mma_all(fr[1], acc);
 }
 
 // Phase 2 of the epilogue for a Q or K head, iteration it: the lane's
@@ -307,23 +338,32 @@ void qkv_gemm_publish(const QkvParams p) {
   // no load leaves w or x.
   const char* wbase = reinterpret_cast<const char*>(p.w + (int64_t)wrow0 * p.hidden);
   const char* xbase = reinterpret_cast<const char*>(p.x + (int64_t)t0 * p.x_stride);
+  const bool loader = wave < LW;
+  const int lw = wave % LW;
   uint32_t aoff[A_DMA], boff[B_DMA];
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int r = 16 * (8 * u + wave) + (lane >> 2);
+  for (int u = 0; u < A_DMA; ++u) {
+    const int r = 16 * (LW * u + lw) + (lane >> 2);
     const int lc = (lane & 3) ^ ((r >> 2) & 3);
     const int wr = min(wrow0 + r, (gh_last + 1) * D - 1) - wrow0;
-    const int xr = min(t0 + r, p.n_tok - 1) - t0;
     aoff[u] = (uint32_t)(wr * p.hidden * 2 + lc * 16);
+  }
+#pragma unroll
+  for (int u = 0; u < B_DMA; ++u) {
+    const int r = 16 * (LW * u + lw) + (lane >> 2);
+    const int lc = (lane & 3) ^ ((r >> 2) & 3);
+    const int xr = min(t0 + r, p.n_tok - 1) - t0;
     boff[u] = (uint32_t)(xr * (int)p.x_stride * 2 + lc * 16);
   }
-  const uint32_t wave_lds = (uint32_t)(uintptr_t)lds + (uint32_t)wave * 1024u;
+  const uint32_t wave_lds = (uint32_t)(uintptr_t)lds + (uint32_t)lw * 1024u;
 
   const int ktiles = p.hidden / TK;
   // tiles 0 .. 2
-  load_tile_at(wbase, xbase, 0, ktiles, aoff, boff, wave_lds);
-  load_tile_at(wbase, xbase, 1, ktiles, aoff, boff, wave_lds);
-  load_tile_at(wbase, xbase, 2, ktiles, aoff, boff, wave_lds);
+  if (loader) {
+    load_tile_at(wbase, xbase, 0, ktiles, aoff, boff, wave_lds);
+    load_tile_at(wbase, xbase, 1, ktiles, aoff, boff, wave_lds);
+    load_tile_at(wbase, xbase, 2, ktiles, aoff, boff, wave_lds);
+  }
 
   // ---- rotary factor table (while the first tiles load) ---------------------
   // the block needs it if its first head is Q or K (heads are section-major)
@@ -406,34 +446,10 @@ void qkv_gemm_publish(const QkvParams p) {
   const int xo[2] = {(hg ^ sw) << 4, ((2 + hg) ^ sw) << 4};
   const int ra = (128 * wm + ql) * ROWB;
   const int rbo = A_BYTES + (64 * wn + ql) * ROWB;
-  Frags fr[2];
-
-  // tile 0: visible after this thread's loads of it are done and the barrier
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * DMAS) : "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-  load_tile_at(wbase, xbase, NSL - 1, ktiles, aoff, boff, wave_lds);
-  read_frag<0>(fr[0], lds, ra, rbo, xo);
-  read_frag<1>(fr[0], lds, ra, rbo, xo);
-  read_frag<2>(fr[0], lds, ra, rbo, xo);
-  read_frag<3>(fr[0], lds, ra, rbo, xo);
-  read_frag<4>(fr[0], lds, ra, rbo, xo);
-  read_frag<5>(fr[0], lds, ra, rbo, xo);
-  read_frag<6>(fr[0], lds, ra, rbo, xo);
-  read_frag<7>(fr[0], lds, ra, rbo, xo);
-  read_frag<8>(fr[0], lds, ra, rbo, xo);
-  read_frag<9>(fr[0], lds, ra, rbo, xo);
-  read_frag<10>(fr[0], lds, ra, rbo, xo);
-  read_frag<11>(fr[0], lds, ra, rbo, xo);
-
-  // steps 0 .. ktiles-2 (tile m's fragments in buffer m % 2), then the
-  // products of the last tile; ktiles = hidden / 32 is even
-  for (int kt = 0; kt < ktiles - 2; kt += 2) {
-    k_step<0>(kt, ktiles, lds, wbase, xbase, aoff, boff, wave_lds, ra, rbo, xo, fr, acc);
-    k_step<1>(kt + 1, ktiles, lds, wbase, xbase, aoff, boff, wave_lds, ra, rbo, xo, fr, acc);
-  }
-  k_step<0>(ktiles - 2, ktiles, lds, wbase, xbase, aoff, boff, wave_lds, ra, rbo, xo, fr, acc);
-  mma_all(fr[1], acc);
+  if (loader)
+    k_loop<true>(ktiles, lds, wbase, xbase, aoff, boff, wave_lds, ra, rbo, xo, acc);
+  else
+    k_loop<false>(ktiles, lds, wbase, xbase, aoff, boff, wave_lds, ra, rbo, xo, acc);
   // the loads of the re-loaded tiles past the last one land in slots no one
   // reads; they complete before the staging area is written
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
