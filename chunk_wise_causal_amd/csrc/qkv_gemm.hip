@@ -17,7 +17,8 @@
 // head) x 64 tokens, eight 32x32 accumulators per wave (two waves per SIMD).
 // Per k-step of 16 a wave reads 6 fragments for 8 products.  k-tiles of 32
 // go straight from global memory into a four-slot LDS ring
-// (global_load_lds_dwordx4, three tiles in flight, 32 KB per tile), 16-byte
+// (global_load_lds_dwordx4, three tiles in flight, 32 KB per tile), issued
+// by one wave per SIMD while the other keeps the matrix pipe fed; 16-byte
 // chunks of the 64-byte rows XOR-swizzled so that the fragment reads of 16
 // consecutive rows hit distinct banks; one barrier per k-tile.  Per CU and
 // clock the block needs 32 bytes of L2 traffic at the full matrix rate, half
@@ -331,11 +332,12 @@ void qkv_gemm_publish(const QkvParams p) {
   const int gh_last = 3 * p.heads - 1;
   const int wrow0 = gh0 * D;                        // first W row of the block
 
-  // ---- load addressing: instruction u of this thread fills LDS row
-  // r = 16 (8u + wave) + lane / 4, physical chunk lane % 4, which holds the
-  // logical chunk (lane % 4) ^ ((r >> 2) & 3) of row r.  Rows past the last
-  // head or token re-read the last one (their results are never stored), so
-  // no load leaves w or x.
+  // ---- load addressing (loading waves lw = 0 .. LW-1): instruction u of a
+  // loading thread fills LDS row r = 16 (LW u + lw) + lane / 4 of its operand,
+  // physical chunk lane % 4, which holds the logical chunk
+  // (lane % 4) ^ ((r >> 2) & 3) of row r.  Rows past the last head or token
+  // re-read the last one (their results are never stored), so no load leaves
+  // w or x.
   const char* wbase = reinterpret_cast<const char*>(p.w + (int64_t)wrow0 * p.hidden);
   const char* xbase = reinterpret_cast<const char*>(p.x + (int64_t)t0 * p.x_stride);
   const bool loader = wave < LW;
