@@ -179,7 +179,7 @@ def _lse(lse: torch.Tensor, H: int, rows: int, exact: bool) -> int:
     if lse.shape[0] != H or (lse.shape[1] != rows if exact else lse.shape[1] < rows):
         want = f"[{H}, {rows}]" if exact else f"[{H}, >= {rows}]"
         raise ValueError(f"lse: expected {want}, got {list(lse.shape)}")
-    if exact and lse.stride(0) != rows:
+    if exact and rows > 0 and lse.stride(0) != rows:   # (torch gives [H, 0] a stride of 1)
         raise ValueError("lse: expected a contiguous [heads, rows] tensor")
     return lse.stride(0)
 

@@ -200,6 +200,10 @@ def test_binding_checks_attention_args(no_lib):
         args.update(kw)
         with pytest.raises(ValueError, match=msg):
             wf.wf_chunk_attn(P, segs, args["q"], qss, out=args["out"], lse=args["lse"])
+    # no rows at all: an empty [H, 0] lse passes the shape checks (torch gives
+    # it a row stride of 1); only the host-resident pool is refused
+    with pytest.raises(ValueError, match="GPU tensor"):
+        wf.wf_chunk_attn(P, segs, q, [0, 0, 0], lse=torch.zeros(2, 0))
     with pytest.raises(ValueError, match="lse"):
         wf.wf_group_attn(P, [(0, 40)], [(0, 40, 0, 1)], q, lse=torch.zeros(2, 30))
     with pytest.raises(ValueError, match="rows"):

@@ -162,3 +162,46 @@ def test_segments_with_gaps_and_any_order():
                                ref["q"], c.q_slot_start(), 0, c.scale, c.dtype)
     mx, rr = G.err_stats(G.to_f64(out), o_ref)
     assert mx <= G.MAX_ABS and rr <= G.REL_RMS
+
+
+def test_degenerate_calls():
+    """Edge cases of the slot layout: a publish of zero tokens leaves the pool
+    untouched; slots with no rows (first, middle and last) and a slot of one
+    row give the oracle's rows for the others and write nothing else; a call
+    with no rows at all writes nothing."""
+    cfg = medium(seed=34)
+    wl = make_workload(cfg)
+    c = wl.cfg
+    ref = oracle_layer(wl)
+    pool, q, _ = G.gpu_layer(wl)
+    k_before, v_before = pool.k_pages.clone(), pool.v_pages.clone()
+    wf.wf_kv_publish(pool, wl.k[:0].to(G.DEV), wl.v[:0].to(G.DEV), 0,
+                     pos=torch.zeros((0, 3), dtype=torch.int32, device=G.DEV),
+                     rope=(c.rope, c.theta))
+    torch.cuda.synchronize()
+    assert torch.equal(pool.k_pages.view(torch.int16), k_before.view(torch.int16))
+    assert torch.equal(pool.v_pages.view(torch.int16), v_before.view(torch.int16))
+    qs = c.q_slot_start()
+    C = qs[1] - qs[0]
+    # slot 0 empty, slot 1 one row, slot 2 empty, slot 3 its full chunk
+    layouts = {
+        "empty_first_one_row": [0, 0, 1, 1, 1 + C],
+        "empty_last": [0, C, 2 * C, 3 * C, 3 * C],
+        "no_rows": [0, 0, 0, 0, 0],
+    }
+    from oracle.attention import chunk_attention
+    for name, lay in layouts.items():
+        print(f"[case] {name}: q_slot_start {lay}", flush=True)
+        n = lay[-1]
+        rows = q[:max(n, 1)].contiguous()
+        out, lse = G.attn(wl, pool, rows, q_slot_start=lay)
+        assert wf.wf_device_status() == 0
+        if n == 0:
+            assert torch.isnan(out).all() and torch.isnan(lse).all()
+            continue
+        o_ref, l_ref = chunk_attention(ref["k_pool"], ref["v_pool"], wl.page_table, c.page_size,
+                                       c.segments(), ref["q"][:n], lay, 0, c.scale, c.dtype)
+        mx, rr = G.err_stats(G.to_f64(out[:n]), o_ref)
+        assert mx <= G.MAX_ABS and rr <= G.REL_RMS, (name, mx, rr)
+        np.testing.assert_allclose(G.to_f64(lse)[:, :n], l_ref, rtol=0,
+                                   atol=G.lse_atol(c.dtype))
