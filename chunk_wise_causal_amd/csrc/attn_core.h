@@ -33,13 +33,16 @@
 //                 tile j+1 is taken while O += P(j) V(j) runs, so the
 //                 probabilities of a tile never wait for a reduction.  The
 //                 denominator sums the bf16-rounded probabilities that
-//                 multiply V (v_dot2 against 1.0), so the weights applied to
-//                 V are normalized exactly.
+//                 multiply V, so the weights applied to V are normalized
+//                 exactly.
 //   O^T += V^T P^T  A = V^T read from the d-major V pages via LDS, B = P^T
 //                 straight from the S^T accumulators: the K rows of S^T are
 //                 loaded in the order sigma(i) (bits 2 and 3 of the row index
 //                 swapped) so that each lane's 8 probabilities of a k-step
-//                 are 8 consecutive keys, matching a 16-byte V^T read.
+//                 are 8 consecutive keys, matching a 16-byte V^T read.  The
+//                 row sums of P ride along on the matrix core: one 16x16x32
+//                 product per k-step of the same P^T fragment against a
+//                 constant 0/1 selector leaves each lane its query's sum.
 //
 // Pipeline: a ring of four LDS slots each for K and V (and the policy's
 // extra slots), filled by direct global->LDS loads (global_load_lds_dwordx4)
@@ -66,6 +69,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int NW = 8;       // waves per block, 32 query rows each
 constexpr int BM = 32 * NW; // query rows per block
@@ -311,15 +315,11 @@ __device__ __forceinline__ float tile_max(const f32x16* s, float sl2) {
   return xhalf_max(mx) * sl2;
 }
 
-// bf16 probabilities of one tile for running max m, and their sum (over the
-// rounded values, via v_dot2 against 1.0)
+// bf16 probabilities of one tile for running max m (their row sums are
+// taken on the matrix core with the P V product, see pv)
 template <int D>
-__device__ __forceinline__ void probs(const f32x16* s, float sl2, float m, bf16x8* pb,
-                                      float* lsum) {
+__device__ __forceinline__ void probs(const f32x16* s, float sl2, float m, bf16x8* pb) {
   const float neg_m = -m;
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-  lsum[0] = 0.f;
-  lsum[1] = 0.f;
 #pragma unroll
   for (int t = 0; t < Frag<D>::PK; ++t) {
     uint32_t pk[4];
@@ -329,22 +329,37 @@ __device__ __forceinline__ void probs(const f32x16* s, float sl2, float m, bf16x
                        __builtin_amdgcn_exp2f(fmaf(s[t >> 1][8 * (t & 1) + 2 * j + 1], sl2, neg_m))};
       const bf16x2 b = __builtin_convertvector(x, bf16x2);
       pk[j] = __builtin_bit_cast(uint32_t, b);
-      lsum[j & 1] = __builtin_amdgcn_fdot2_f32_bf16(b, ones, lsum[j & 1], false);
     }
     pb[t] = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
   }
 }
 
+// Row-sum selector: the A operand of a 16x16x32 product whose B operand is
+// the P^T fragment of a k-step.  Read as a 16x16x32 B operand, lane
+// 16g + n of that fragment holds 8 keys of query n + 16 (g % 2); row m of
+// the selector is 1 on the k-groups g with g % 2 == (m / 4) % 2, so every
+// output register of lane l is the sum of the k-step's 16 probabilities of
+// query l % 32, the query the lane holds in S^T and O^T.
+__device__ __forceinline__ bf16x8 rowsum_selector(int lane) {
+  const int m = lane & 15, g = lane >> 4;
+  const uint32_t w = ((g & 1) == ((m >> 2) & 1)) ? 0x3f803f80u : 0u;   // bf16 1.0 pairs
+  return __builtin_bit_cast(bf16x8, make_uint4(w, w, w, w));
+}
+
+// O^T += V^T P^T, and l += the row sums of the same bf16 probabilities on
+// the matrix core (one 16x16x32 product per k-step against the selector)
 template <int D>
 __device__ __forceinline__ void pv(const uint16_t* __restrict__ vbuf, const int* vaddr,
-                                   const bf16x8* pb, f32x16* o) {
+                                   const bf16x8* pb, f32x16* o, const bf16x8& sel, f32x4& lacc) {
 #pragma unroll
-  for (int t = 0; t < Frag<D>::PK; ++t)
+  for (int t = 0; t < Frag<D>::PK; ++t) {
 #pragma unroll
     for (int db = 0; db < Frag<D>::DB; ++db) {
       const bf16x8 a = *reinterpret_cast<const bf16x8*>(vbuf + vaddr[t] + 32 * db * BN);
       o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[t], o[db], 0, 0, 0);
     }
+    lacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel, pb[t], lacc, 0, 0, 0);
+  }
 }
 
 // Scheduling hint for the block of O += P(j) V(j) and the max of S(j+1):
@@ -352,7 +367,7 @@ __device__ __forceinline__ void pv(const uint16_t* __restrict__ vbuf, const int*
 // one vector instruction of the max.
 template <int D>
 __device__ __forceinline__ void interleave_pv_max() {
-  constexpr int NM = Frag<D>::PK * Frag<D>::DB;   // MFMAs of the product
+  constexpr int NM = Frag<D>::PK * (Frag<D>::DB + 1);   // MFMAs of the product and row sums
   constexpr int AHEAD = 3;
 #pragma unroll
   for (int k = 0; k < AHEAD; ++k) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
@@ -386,9 +401,10 @@ __device__ __forceinline__ void mask_tile(f32x16* s, int kt, int w_lo, int w_hi,
 // exceeds it by more than the slack; the caller then rescales O and l.
 template <int D>
 __device__ __forceinline__ bool pv_max(const uint16_t* __restrict__ vbuf, const int* vaddr,
-                                       const bf16x8* pb, f32x16* o, const f32x16* s_nxt,
-                                       float m_run, float sl2, float& m_new) {
-  pv<D>(vbuf, vaddr, pb, o);
+                                       const bf16x8* pb, f32x16* o, const bf16x8& sel,
+                                       f32x4& lacc, const f32x16* s_nxt, float m_run, float sl2,
+                                       float& m_new) {
+  pv<D>(vbuf, vaddr, pb, o, sel, lacc);
   const float mt = tile_max<D>(s_nxt, sl2);
   interleave_pv_max<D>();
   m_new = fmaxf(m_run, mt);
@@ -397,10 +413,9 @@ __device__ __forceinline__ bool pv_max(const uint16_t* __restrict__ vbuf, const 
 
 // Raise the running max to m_new: O and l scale by 2^(m_run - m_new).
 template <int D>
-__device__ __forceinline__ void rescale(f32x16* o, float* l_acc, float& m_run, float m_new) {
+__device__ __forceinline__ void rescale(f32x16* o, f32x4& lacc, float& m_run, float m_new) {
   const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-  l_acc[0] *= alpha;
-  l_acc[1] *= alpha;
+  lacc *= alpha;
 #pragma unroll
   for (int i = 0; i < Frag<D>::DB; ++i) o[i] *= alpha;
   m_run = m_new;
@@ -453,6 +468,7 @@ struct Loop {
     int head, rng1, hg;
     float sl2;
     const int* vaddr;
+    bf16x8 sel;         // row-sum selector (rowsum_selector)
   };
 
   static __device__ __forceinline__ const uint16_t* vslot(const uint16_t* lds, int i) {
@@ -468,17 +484,12 @@ struct Loop {
   // block of MFMAs and vector work.
   template <int NK>
   static __device__ __forceinline__ void softmax_qk(const Args& a, const f32x16* s_cur,
-                                                    f32x16* s_nxt, float m_run, float* l_acc,
-                                                    bf16x8* pb) {
+                                                    f32x16* s_nxt, float m_run, bf16x8* pb) {
     S::template qk<D, NK * KSLOT, XBASE + NK * XSLOT>(a.lds, a.kc, s_nxt);
-    float lsum[2];
-    probs<D>(s_cur, a.sl2, m_run, pb, lsum);
+    probs<D>(s_cur, a.sl2, m_run, pb);
 #pragma unroll
     for (int t = 0; t < Frag<D>::PK; ++t) asm volatile("" ::"v"(pb[t]));
-    asm volatile("" ::"v"(lsum[0]), "v"(lsum[1]));
     S::template interleave_qk_softmax<D>();
-    l_acc[0] += lsum[0];
-    l_acc[1] += lsum[1];
   }
 
   // Step j with J = j mod NS.  Scores of tile j are in s_cur.  Returns false
@@ -489,7 +500,7 @@ struct Loop {
   static __device__ __forceinline__ bool step(const Args& a, Walk& wk, Tile* tl, int& bad_u,
                                               int& bad_v, int& last, f32x16* s_cur,
                                               f32x16* s_nxt, bf16x8* pb, f32x16* o,
-                                              float& m_run, float* l_acc) {
+                                              float& m_run, f32x4& lacc) {
     const Tile tj = tl[J];   // tile j: its window masks S(j)
     // the page read issued by the last step lands here, before any LDS read
     // is in flight: a pending scalar load inside the compute block would
@@ -510,7 +521,7 @@ struct Loop {
       tile_window(a.p, tj, lo, hi);
       mask_tile<D>(s_cur, tile_kt(tj), lo, hi, a.hg);
     }
-    softmax_qk<(J + 1) % NS>(a, s_cur, s_nxt, m_run, l_acc, pb);
+    softmax_qk<(J + 1) % NS>(a, s_cur, s_nxt, m_run, pb);
     if (tl[(J + 1) % NS].ktc < 0) {
       last = J;   // P(j) V(j) of the last tile runs after the loop
       return false;
@@ -518,8 +529,8 @@ struct Loop {
     const uint16_t* vb = vslot(a.lds, J);
     float m_new;
     if (!LAG) {
-      if (pv_max<D>(vb, a.vaddr, pb, o, s_nxt, m_run, a.sl2, m_new))
-        rescale<D>(o, l_acc, m_run, m_new);
+      if (pv_max<D>(vb, a.vaddr, pb, o, a.sel, lacc, s_nxt, m_run, a.sl2, m_new))
+        rescale<D>(o, lacc, m_run, m_new);
       tl[J] = walk_tile<BP>(a.p, a.rng1, wk, bad_u);   // tile j+4
       walk_next<BP>(a.p, a.rng1, wk);
     }
@@ -529,14 +540,14 @@ struct Loop {
     if (!LAG) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(DMAS) : "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (LAG && pv_max<D>(vb, a.vaddr, pb, o, s_nxt, m_run, a.sl2, m_new))
-      rescale<D>(o, l_acc, m_run, m_new);
+    if (LAG && pv_max<D>(vb, a.vaddr, pb, o, a.sel, lacc, s_nxt, m_run, a.sl2, m_new))
+      rescale<D>(o, lacc, m_run, m_new);
     return true;
   }
 
   template <bool LAG>
   static __device__ __forceinline__ void run(const Args& a, int rng0, f32x16* o, float& m_run,
-                                             float* l_acc, int& bad_u, int& bad_v) {
+                                             f32x4& lacc, int& bad_u, int& bad_v) {
     // prologue: the walk's first four tiles, K(0..2), V(0..1), then S(0)
     // and the first running max (step 0 loads K(3))
     Walk wk = walk_first<BP>(a.p, rng0);
@@ -577,14 +588,14 @@ struct Loop {
     int last = 0;
     while (true) {
 #define WF_STEP(J, SC, SN)                                                                   \
-  if (!step<J, LAG>(a, wk, tl, bad_u, bad_v, last, SC, SN, pb, o, m_run, l_acc)) break;
+  if (!step<J, LAG>(a, wk, tl, bad_u, bad_v, last, SC, SN, pb, o, m_run, lacc)) break;
       WF_STEP(0, sa, sb)
       WF_STEP(1, sb, sa)
       WF_STEP(2, sa, sb)
       WF_STEP(3, sb, sa)
 #undef WF_STEP
     }
-    pv<D>(vslot(a.lds, last), a.vaddr, pb, o);
+    pv<D>(vslot(a.lds, last), a.vaddr, pb, o, a.sel, lacc);
     // no LDS-DMA may still be in flight when the block ends
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
@@ -650,21 +661,22 @@ __device__ __forceinline__ void attn_body(const AttnParams& p, const typename S:
 #pragma unroll
   for (int i = 0; i < DB; ++i) o[i] = f32x16{};
   float m_run;               // running max of scale*log2(e)*<q,k>
-  float l_acc[2] = {0.f, 0.f};
+  f32x4 lacc = {0.f, 0.f, 0.f, 0.f};   // row sums of P (every register: the lane's query)
   int bad_u = 0, bad_v = 0;  // bad page entries: wave-uniform and per-lane
-  const typename L::Args args{p, kc, lc, lds, head, rng1, hg, p.scale_log2, vaddr};
+  const typename L::Args args{p, kc, lc, lds, head, rng1, hg, p.scale_log2, vaddr,
+                              rowsum_selector(lane)};
   // waves NW/2.. run half a tile behind (see Loop)
   if (wave >= NW / 2)
-    L::template run<true>(args, rng0, o, m_run, l_acc, bad_u, bad_v);
+    L::template run<true>(args, rng0, o, m_run, lacc, bad_u, bad_v);
   else
-    L::template run<false>(args, rng0, o, m_run, l_acc, bad_u, bad_v);
+    L::template run<false>(args, rng0, o, m_run, lacc, bad_u, bad_v);
   // one status write per wave that met a bad page entry (per-lane lookups
   // of the register path included)
   if ((bad_u | (__builtin_amdgcn_ballot_w64(bad_v != 0) != 0)) && lane == 0)
     atomicOr(p.status, WF_STATUS_BAD_PAGE);
 
   // ---- epilogue: O = O^T / l, LSE ------------------------------------------
-  const float l = xhalf_sum(l_acc[0] + l_acc[1]);
+  const float l = lacc[0];
   const float inv = 1.0f / l;
   if (qvalid) {
     uint16_t* op = static_cast<uint16_t*>(p.out) + (int64_t)qrow * p.out_stride + head * D;
