@@ -46,6 +46,9 @@ SHAPES = {
     "fp32_d128_ps64": small_config(dtype="fp32", page_size=64, seed=13),
     "w1_dense": medium(slots=1, seed=25),
     "w6_ps16": small_config(slots=6, frames_per_chunk=1, seed=14),
+    # chunk 360 = 256 + 104: a short partial last query tile in every slot
+    "medium_packed_ps64": medium(frame_cols=12, seed=26),
+    "medium_packed_w5_ps256": medium(frame_cols=12, slots=5, page_size=256, seed=27),
 }
 
 
@@ -120,8 +123,11 @@ def test_plain_scatter_and_unaligned_window():
     assert np.array_equal(G.bits(G.to_storage(pool.v_pages)), G.bits(vp))
 
 
-def test_first_slot_share_equals_full_call():
-    wl = make_workload(medium(seed=32))
+@pytest.mark.parametrize("cols", [13, 12], ids=["chunk390", "chunk360_packed"])
+def test_first_slot_share_equals_full_call(cols):
+    """One slot per call equals that slot's rows of the full call, bit for
+    bit (chunk 390 and 360: partial last query tiles of 134 and 104 rows)."""
+    wl = make_workload(medium(frame_cols=cols, seed=32))
     c = wl.cfg
     pool, q, _ = G.gpu_layer(wl)
     full, lse_full = G.attn(wl, pool, q)
