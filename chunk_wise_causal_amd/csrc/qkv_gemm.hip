@@ -126,6 +126,16 @@ __device__ __forceinline__ void mma(const Frags& f, f32x16 (&acc)[4][2]) {
   acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[ks][i], f.b[ks][j], acc[i][j], 0, 0, 0);
 }
 
+// A wave-uniform pointer, held in scalar registers: the base operand of the
+// direct loads must be a scalar register pair, which the compiler cannot
+// choose on its own once it has placed the value in vector registers.
+__device__ __forceinline__ const char* uniform_ptr(const char* q) {
+  const uint64_t u = reinterpret_cast<uint64_t>(q);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return reinterpret_cast<const char*>(((uint64_t)hi << 32) | lo);
+}
+
 // the scheduler keeps the source order across this point
 __device__ __forceinline__ void fence() { __builtin_amdgcn_sched_barrier(0); }
 
@@ -269,16 +279,16 @@ __device__ __forceinline__ void k_loop(int ktiles, const char* lds, const char* 
   mma_all(fr[1], acc);
 }
 
-// Phase 2 of the epilogue for a Q or K head, iteration it: the lane's
-// 16-byte chunk c of token 64 wn + 4 it + lane / 16 is read from the stage,
-// rotated (MODE 0: no rotation, 1: factors from the block's table, 2:
-// factors evaluated per element) and stored to its Q row or K page row.
-template <int MODE>
+// Phase 2 of the epilogue for a Q (SEC 0) or K (SEC 1) head, iteration it:
+// the lane's 16-byte chunk c of token 64 wn + 4 it + lane / 16 is read from
+// the stage, rotated (MODE 0: no rotation, 1: factors from the block's
+// table, 2: factors evaluated per element) and stored to its Q row or K page
+// row.
+template <int MODE, int SEC>
 __device__ __forceinline__ void qk_store(const QkvParams& p, int it, int lane, int wn, int t0,
                                          int pg, int c, const int* ax, const int* rbq,
                                          const char* stage, const int4* post,
-                                         const float2* tab, int sec, int head, int ps,
-                                         int& bad) {
+                                         const float2* tab, int head, int ps, int& bad) {
   const int tk = 4 * it + (lane >> 4);
   const int tt = 64 * wn + tk;
   const int t = t0 + tt;
@@ -299,7 +309,7 @@ __device__ __forceinline__ void qk_store(const QkvParams& p, int it, int lane, i
       wv[q] = pack_bf16x2(y0, y1);
     }
   }
-  if (sec == 0) {
+  if (SEC == 0) {
     *reinterpret_cast<uint4*>(p.q_out + (int64_t)t * p.q_stride + head * D + c * 8) = v;
   } else {
     const int L = p.dst_start + t;
@@ -309,6 +319,115 @@ __device__ __forceinline__ void qk_store(const QkvParams& p, int it, int lane, i
     }
     *reinterpret_cast<uint4*>(p.k_pages + (((int64_t)page * p.heads + head) * ps + (L & (ps - 1))) * D +
                               c * 8) = v;
+  }
+}
+
+// The epilogue of a wave whose head is in section SEC (0 Q, 1 K, 2 V), one
+// copy per section so that neither phase branches on it.  Phase 1: the
+// wave's 64 tokens of its head, + bias and rounded to bf16 (the unfused
+// projection's output), into the stage (the ring's LDS).  Phase 2: the wave
+// re-reads its own part in the output's order; Q and K are rotated there
+// (the accumulators are dead by then), and every global store is 16 bytes.
+// bias2[4 i + q4] holds the bias of the lane's features 32 i + 8 q4 + 4 hg
+// .. + 3 (bf16 pairs).
+template <int SEC>
+__device__ __forceinline__ void epilogue(const QkvParams& p, const f32x16 (&acc)[4][2],
+                                         const uint2* bias2, int lane, int ql, int hg, int wn,
+                                         int t0, int pg, bool use_tab, const int* rbt,
+                                         char* stage, const int4* post, const float2* tab,
+                                         int head, int ps, int& bad) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      // features fl .. fl+3 of the head: registers 4 q4 .. 4 q4 + 3
+      const int fl = 32 * i + 8 * q4 + 4 * hg;
+      const uint2 b2 = bias2[4 * i + q4];
+      const float bv[4] = {__uint_as_float(b2.x << 16), __uint_as_float(b2.x & 0xffff0000u),
+                           __uint_as_float(b2.y << 16), __uint_as_float(b2.y & 0xffff0000u)};
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const uint32_t lo = pack_bf16x2(acc[i][j][4 * q4] + bv[0], acc[i][j][4 * q4 + 1] + bv[1]);
+        const uint32_t hi =
+            pack_bf16x2(acc[i][j][4 * q4 + 2] + bv[2], acc[i][j][4 * q4 + 3] + bv[3]);
+        const int tt = 64 * wn + 32 * j + ql;   // token of the block
+        if (SEC < 2) {
+          // [token][feature] rows of 256 bytes, 16-byte chunks swizzled by token
+          *reinterpret_cast<uint2*>(stage + tt * 256 + ((((fl >> 3) ^ tt) & 15) << 4) +
+                                    (hg << 3)) = make_uint2(lo, hi);
+        } else {
+          // [feature][token] rows of 512 bytes
+          uint16_t* col = reinterpret_cast<uint16_t*>(stage + fl * (BN * 2) + tt * 2);
+          col[0] = (uint16_t)lo;
+          col[BN] = (uint16_t)(lo >> 16);
+          col[2 * BN] = (uint16_t)hi;
+          col[3 * BN] = (uint16_t)(hi >> 16);
+        }
+      }
+    }
+  // the wave re-reads only what it wrote: LDS operations of one wave complete
+  // in order, and the wait keeps the compiler from moving the reads up
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+
+  if (SEC < 2) {
+    // 64 tokens x 16 chunks of 8 features: lane -> (token, chunk); the
+    // chunk c = lane % 16 is the same in every iteration, and with it the
+    // lane's 4 pairs, their axes and table rows
+    const int c = lane & 15;
+    int ax[4] = {0, 0, 0, 0}, rbq[4] = {0, 0, 0, 0};
+    if (p.rope) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        ax[q] = axis_of(p, 4 * c + q);
+        if (use_tab) rbq[q] = rbt[4 * c + q];
+      }
+    }
+    // the rotation mode picks one of three copies of the loop: unrolled for
+    // no rotation and for table factors, rolled for per-element factors
+    if (!p.rope) {
+#pragma unroll
+      for (int it = 0; it < 16; ++it)
+        qk_store<0, SEC>(p, it, lane, wn, t0, pg, c, ax, rbq, stage, post, tab, head, ps, bad);
+    } else if (use_tab) {
+#pragma unroll
+      for (int it = 0; it < 16; ++it)
+        qk_store<1, SEC>(p, it, lane, wn, t0, pg, c, ax, rbq, stage, post, tab, head, ps, bad);
+    } else {
+#pragma unroll 1
+      for (int it = 0; it < 16; ++it)
+        qk_store<2, SEC>(p, it, lane, wn, t0, pg, c, ax, rbq, stage, post, tab, head, ps, bad);
+    }
+  } else {
+    // 128 features x 8 runs of 8 tokens: lane -> (feature, run)
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+      const int idx = it * 64 + lane;
+      const int fr = idx >> 3, tt = 64 * wn + 8 * (idx & 7);
+      const int t = t0 + tt;
+      const int L = p.dst_start + t;
+      const char* src = stage + fr * (BN * 2) + tt * 2;
+      const int page = __shfl(pg, 8 * (idx & 7));   // every lane active here
+      if (t + 8 <= p.n_tok && (L & 7) == 0) {
+        // 8 consecutive tokens of one page (pages hold a multiple of 8)
+        if ((unsigned)page >= (unsigned)p.num_pages) {
+          bad = 1;
+          continue;
+        }
+        *reinterpret_cast<uint4*>(p.v_pages + (((int64_t)page * p.heads + head) * D + fr) * ps +
+                                  (L & (ps - 1))) = *reinterpret_cast<const uint4*>(src);
+      } else {
+        for (int u = 0; u < 8 && t + u < p.n_tok; ++u) {
+          const int Lu = L + u;
+          const int pgu = p.page_table[Lu >> p.ps_log2];
+          if ((unsigned)pgu >= (unsigned)p.num_pages) {
+            bad = 1;
+            continue;
+          }
+          p.v_pages[(((int64_t)pgu * p.heads + head) * D + fr) * ps + (Lu & (ps - 1))] =
+              reinterpret_cast<const uint16_t*>(src)[u];
+        }
+      }
+    }
   }
 }
 
@@ -338,8 +457,8 @@ void qkv_gemm_publish(const QkvParams p) {
   // (lane % 4) ^ ((r >> 2) & 3) of row r.  Rows past the last head or token
   // re-read the last one (their results are never stored), so no load leaves
   // w or x.
-  const char* wbase = reinterpret_cast<const char*>(p.w + (int64_t)wrow0 * p.hidden);
-  const char* xbase = reinterpret_cast<const char*>(p.x + (int64_t)t0 * p.x_stride);
+  const char* wbase = uniform_ptr(reinterpret_cast<const char*>(p.w + (int64_t)wrow0 * p.hidden));
+  const char* xbase = uniform_ptr(reinterpret_cast<const char*>(p.x + (int64_t)t0 * p.x_stride));
   const bool loader = wave < LW;
   const int lw = wave % LW;
   uint32_t aoff[A_DMA], boff[B_DMA];
@@ -457,10 +576,6 @@ void qkv_gemm_publish(const QkvParams p) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // ---- epilogue ----------------------------------------------------------------
-  // Phase 1: every wave writes its 64 tokens of its head, + bias and rounded
-  // to bf16, into the stage (the ring's LDS).  Phase 2: the wave re-reads its
-  // own part in the output's order; Q and K are rotated there (the
-  // accumulators are dead by then), and every global store is 16 bytes.
   __syncthreads();   // every wave is done with the ring: it becomes the stage
   const int hs = 2 * tl.ftile + wm;   // this wave's head among the computed ones
   if (hs >= n_heads) return;
@@ -468,7 +583,6 @@ void qkv_gemm_publish(const QkvParams p) {
   const int sec = gh / p.heads, head = gh - sec * p.heads;
   char* stage = lds + wm * (RING / 2);
   const int ps = 1 << p.ps_log2;
-  const bool bias8 = p.bias && (reinterpret_cast<uintptr_t>(p.bias) & 7) == 0;
   // K and V: the page of the wave's token 64 wn + lane, read before phase 1
   // so that its latency hides behind it; phase 2 takes a token's page from
   // its lane (one dependent table read per token instead of per store)
@@ -477,113 +591,35 @@ void qkv_gemm_publish(const QkvParams p) {
     const int t = t0 + 64 * wn + lane;
     if (t < p.n_tok) pg = p.page_table[(p.dst_start + t) >> p.ps_log2];
   }
-
+  // the bias of the lane's 64 features, as bf16 pairs
+  uint2 bias2[16];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int k = 0; k < 16; ++k) bias2[k] = make_uint2(0u, 0u);
+  if (p.bias) {
+    const uint16_t* bp = p.bias + gh * D + 4 * hg;
+    if ((reinterpret_cast<uintptr_t>(p.bias) & 7) == 0) {
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      // features fl .. fl+3 of the head: registers 4 q4 .. 4 q4 + 3
-      const int fl = 32 * i + 8 * q4 + 4 * hg;
-      float bv[4] = {0.f, 0.f, 0.f, 0.f};
-      if (p.bias) {
-        const uint16_t* bp = p.bias + gh * D + fl;
-        if (bias8) {
-          const uint2 b2 = *reinterpret_cast<const uint2*>(bp);
-          bv[0] = __uint_as_float(b2.x << 16);
-          bv[1] = __uint_as_float(b2.x & 0xffff0000u);
-          bv[2] = __uint_as_float(b2.y << 16);
-          bv[3] = __uint_as_float(b2.y & 0xffff0000u);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) bv[e] = bf16_to_f32(bp[e]);
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const uint32_t lo = pack_bf16x2(acc[i][j][4 * q4] + bv[0], acc[i][j][4 * q4 + 1] + bv[1]);
-        const uint32_t hi =
-            pack_bf16x2(acc[i][j][4 * q4 + 2] + bv[2], acc[i][j][4 * q4 + 3] + bv[3]);
-        const int tt = 64 * wn + 32 * j + ql;   // token of the block
-        if (sec < 2) {
-          // [token][feature] rows of 256 bytes, 16-byte chunks swizzled by token
-          *reinterpret_cast<uint2*>(stage + tt * 256 + ((((fl >> 3) ^ tt) & 15) << 4) +
-                                    (hg << 3)) = make_uint2(lo, hi);
-        } else {
-          // [feature][token] rows of 512 bytes
-          uint16_t* col = reinterpret_cast<uint16_t*>(stage + fl * (BN * 2) + tt * 2);
-          col[0] = (uint16_t)lo;
-          col[BN] = (uint16_t)(lo >> 16);
-          col[2 * BN] = (uint16_t)hi;
-          col[3 * BN] = (uint16_t)(hi >> 16);
-        }
-      }
-    }
-  // the wave re-reads only what it wrote: LDS operations of one wave complete
-  // in order, and the wait keeps the compiler from moving the reads up
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-
-  int bad = 0;
-  if (sec < 2) {
-    const bool rot = p.rope != 0;
-    // 64 tokens x 16 chunks of 8 features: lane -> (token, chunk); the
-    // chunk c = lane % 16 is the same in every iteration, and with it the
-    // lane's 4 pairs, their axes and table rows
-    const int c = lane & 15;
-    int ax[4] = {0, 0, 0, 0}, rbq[4] = {0, 0, 0, 0};
-    if (rot) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        ax[q] = axis_of(p, 4 * c + q);
-        if (use_tab) rbq[q] = rbt[4 * c + q];
-      }
-    }
-    // the rotation mode picks one of three copies of the loop: unrolled for
-    // no rotation and for table factors, rolled for per-element factors
-    if (!rot) {
-#pragma unroll
-      for (int it = 0; it < 16; ++it)
-        qk_store<0>(p, it, lane, wn, t0, pg, c, ax, rbq, stage, post, tab, sec, head, ps, bad);
-    } else if (use_tab) {
-#pragma unroll
-      for (int it = 0; it < 16; ++it)
-        qk_store<1>(p, it, lane, wn, t0, pg, c, ax, rbq, stage, post, tab, sec, head, ps, bad);
+      for (int k = 0; k < 16; ++k)
+        bias2[k] = *reinterpret_cast<const uint2*>(bp + 32 * (k >> 2) + 8 * (k & 3));
     } else {
-#pragma unroll 1
-      for (int it = 0; it < 16; ++it)
-        qk_store<2>(p, it, lane, wn, t0, pg, c, ax, rbq, stage, post, tab, sec, head, ps, bad);
-    }
-  } else {
-    // 128 features x 8 runs of 8 tokens: lane -> (feature, run)
 #pragma unroll
-    for (int it = 0; it < 16; ++it) {
-      const int idx = it * 64 + lane;
-      const int fr = idx >> 3, tt = 64 * wn + 8 * (idx & 7);
-      const int t = t0 + tt;
-      const int L = p.dst_start + t;
-      const char* src = stage + fr * (BN * 2) + tt * 2;
-      const int page = __shfl(pg, 8 * (idx & 7));   // every lane active here
-      if (t + 8 <= p.n_tok && (L & 7) == 0) {
-        // 8 consecutive tokens of one page (pages hold a multiple of 8)
-        if ((unsigned)page >= (unsigned)p.num_pages) {
-          bad = 1;
-          continue;
-        }
-        *reinterpret_cast<uint4*>(p.v_pages + (((int64_t)page * p.heads + head) * D + fr) * ps +
-                                  (L & (ps - 1))) = *reinterpret_cast<const uint4*>(src);
-      } else {
-        for (int u = 0; u < 8 && t + u < p.n_tok; ++u) {
-          const int Lu = L + u;
-          const int page = p.page_table[Lu >> p.ps_log2];
-          if ((unsigned)page >= (unsigned)p.num_pages) {
-            bad = 1;
-            continue;
-          }
-          p.v_pages[(((int64_t)page * p.heads + head) * D + fr) * ps + (Lu & (ps - 1))] =
-              reinterpret_cast<const uint16_t*>(src)[u];
-        }
+      for (int k = 0; k < 16; ++k) {
+        const uint16_t* b = bp + 32 * (k >> 2) + 8 * (k & 3);
+        bias2[k] = make_uint2((uint32_t)b[0] | ((uint32_t)b[1] << 16),
+                              (uint32_t)b[2] | ((uint32_t)b[3] << 16));
       }
     }
   }
+  int bad = 0;
+  if (sec == 0)
+    epilogue<0>(p, acc, bias2, lane, ql, hg, wn, t0, pg, use_tab, rbt, stage, post, tab, head,
+                ps, bad);
+  else if (sec == 1)
+    epilogue<1>(p, acc, bias2, lane, ql, hg, wn, t0, pg, use_tab, rbt, stage, post, tab, head,
+                ps, bad);
+  else
+    epilogue<2>(p, acc, bias2, lane, ql, hg, wn, t0, pg, use_tab, rbt, stage, post, tab, head,
+                ps, bad);
   if (bad) atomicOr(p.status, WF_STATUS_BAD_PAGE);
 }
 
