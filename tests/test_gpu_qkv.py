@@ -89,6 +89,9 @@ CASES = {
     "ps64_one_tile_no_q": (1, 64, 17, 64, 5, True, False, True),
     "ps32_wide_positions": (2, 128, 300, 32, 64, True, True, "wide"),
     "ps16_denormal_outputs": (1, 64, 80, 16, 0, False, True, "denormal"),
+    # bias at an address 2 bytes past an 8-byte boundary: the kernel's
+    # element-wise bias path
+    "ps64_h3_bias_unaligned": (3, 256, 300, 64, 0, "unaligned", True, True),
 }
 
 
@@ -138,8 +141,16 @@ def test_qkv_publish_parity(name):
     pool.k_pages.view(torch.int16).fill_(int(NAN_BF16))     # 0x7FC1: the oracle's NaN fill
     pool.v_pages.view(torch.int16).fill_(int(NAN_BF16))
     q_out = torch.full((n, H, 128), float("nan"), dtype=torch.bfloat16, device=G.DEV) if use_q else None
+    bias = None
+    if use_bias == "unaligned":
+        store = torch.empty(b.numel() + 1, dtype=torch.bfloat16, device=G.DEV)
+        store[1:] = b.to(G.DEV)
+        bias = store[1:]
+        assert bias.data_ptr() % 8 == 2
+    elif use_bias:
+        bias = b.to(G.DEV)
     wf.wf_qkv_publish(pool, x.to(G.DEV), w.to(G.DEV), dst, pos=pos.to(G.DEV) if use_rope else None,
-                      rope=rope, bias=b.to(G.DEV) if use_bias else None, q_out=q_out)
+                      rope=rope, bias=bias, q_out=q_out)
     torch.cuda.synchronize()
     assert wf.wf_device_status() == 0
     kg, vg = G.to_storage(pool.k_pages), G.to_storage(pool.v_pages)
