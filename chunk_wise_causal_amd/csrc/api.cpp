@@ -287,7 +287,13 @@ int publish_impl(const wf_kv_pool* pool, const wf_mx_keys* mx, const wf_rope* ro
   p.num_pages = pool->num_pages;
   p.num_logical_pages = pool->num_logical_pages;
   p.rope = rope ? 1 : 0;
-  if (rope) fill_pairs(rope, p.pair_axis, p.pair_omega);
+  if (rope) {
+    fill_pairs(rope, p.pair_axis, p.pair_omega);
+    p.band0[0] = 0;
+    p.band0[1] = rope->d_t / 2;
+    p.band0[2] = (rope->d_t + rope->d_h) / 2;
+    p.band0[3] = pool->head_dim / 2;
+  }
   // 64-token tiles of the window; K blocks take groups of about 10 heads,
   // split evenly (the rotary factors of a tile are evaluated once per K
   // block), V blocks 256 features (bfloat16) or one head (float32)

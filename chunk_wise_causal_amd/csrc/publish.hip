@@ -24,6 +24,7 @@
 // Pool rows of both kinds are written with device-scope stores (st_device).
 // Token tiles are aligned to 64 in logical space, so an 8-token run never
 // crosses a page (pages hold >= 16 tokens).
+#include <climits>
 #include <type_traits>
 
 #include "../../include/wf.h"
@@ -115,12 +116,27 @@ __device__ __forceinline__ void mx_store(const PublishParams& p, void* k8_scales
     __builtin_nontemporal_store(word, static_cast<uint32_t*>(k8_scales) + idx / D);
 }
 
+// K blocks' factor table of a tile: the tile's token positions, the
+// per-axis position ranges, the table row base of every pair and the
+// (cos, sin) of every (pair, position) present, within the LDS of the
+// per-element factors it replaces
+template <int D>
+struct KTable {
+  // entries that fit the LDS of the per-element factors (32 tokens x D/2 pairs)
+  static constexpr int CAP = (kTileTok / 2 * (D / 2) * 8 - kTileTok * 16 - 8 * 4 - (D / 2) * 4) / 8;
+  int4 pos[kTileTok];
+  int hdr[8];
+  int rb[D / 2];
+  float2 tab[CAP];
+};
+
 template <int D, typename T>
 union PublishShared {
   // LDS row padding (elements): 8 bytes, so that the 8 rows one run reads
   // (8 apart) spread over more banks than with a 16-byte pad
   static constexpr int VPAD = 8 / sizeof(T);
   float2 cs[kTileTok / 2][D / 2];               // K blocks: rotary factors (32 tokens)
+  KTable<D> kt;                                 // K blocks: the tile's factor table
   T vt[kTileTok][D + VPAD];                     // V blocks: staged rows
 };
 
@@ -142,6 +158,155 @@ __device__ __forceinline__ void tile_pages(const PublishParams& p, int L0, int l
     }
     page_of[tid] = page;
   }
+}
+
+// A K block's rotation from a per-tile factor table.  On a frame grid the
+// tile's 64 tokens take few distinct positions per axis, so the factors are
+// evaluated once per (pair, position) present, the per-axis position ranges
+// of the tile's in-window tokens, instead of once per (token, pair); every
+// head of the group then rotates with table lookups in one pass of 64
+// tokens.  The factors are the same double-precision evaluation rounded to
+// float, so the results do not change.  Returns false (nothing done but
+// reading the positions) when the ranges do not fit the table.
+template <int D, bool BF16, bool HAS_Q, bool MX>
+__device__ __forceinline__ bool k_block_table(const PublishParams& p, void* k8_scales,
+                                              KTable<D>& kt, const int* page_of, int L0, int lo,
+                                              int hi, int h0, int h1) {
+  using T = typename std::conditional<BF16, uint16_t, float>::type;
+  constexpr int EPV = 16 / sizeof(T);        // elements per 16-byte vector
+  constexpr int VPR = D / EPV;               // vectors per head row
+  constexpr int NP = D / 2;
+  constexpr int PER = kTileTok * VPR / kThreads;   // vectors per thread per head
+  const int tid = threadIdx.x;
+  const int ps = 1 << p.ps_log2;
+  if (tid < kTileTok) {
+    // wave 0 holds the tile's tokens: positions and per-axis ranges of the
+    // in-window ones (an empty tile leaves hi < lo)
+    const int L = L0 + tid;
+    const bool in = L >= lo && L < hi;
+    int4 v = make_int4(0, 0, 0, 0);
+    if (in) {
+      const int64_t t = L - p.dst_start;
+      v = make_int4(p.pos[t * 3], p.pos[t * 3 + 1], p.pos[t * 3 + 2], 0);
+    }
+    kt.pos[tid] = v;
+    int lo3[3], hi3[3];
+    const int a0[3] = {v.x, v.y, v.z};
+#pragma unroll
+    for (int a = 0; a < 3; ++a) {
+      int mn = in ? a0[a] : INT_MAX, mx = in ? a0[a] : INT_MIN;
+#pragma unroll
+      for (int m = 1; m < 64; m <<= 1) {
+        mn = min(mn, __shfl_xor(mn, m));
+        mx = max(mx, __shfl_xor(mx, m));
+      }
+      lo3[a] = mn;
+      hi3[a] = mx;
+    }
+    if (tid == 0) {
+#pragma unroll
+      for (int a = 0; a < 3; ++a) {
+        kt.hdr[a] = lo3[a];
+        kt.hdr[3 + a] = hi3[a];
+      }
+    }
+  }
+  __syncthreads();   // positions, ranges and page_of visible
+  int64_t rng[3], off[4];
+  int mn[3];
+  off[0] = 0;
+  bool fits = true;
+#pragma unroll
+  for (int a = 0; a < 3; ++a) {
+    mn[a] = kt.hdr[a];
+    rng[a] = (int64_t)kt.hdr[3 + a] - kt.hdr[a] + 1;
+    fits &= rng[a] >= 1;
+    off[a + 1] = off[a] + (int64_t)(p.band0[a + 1] - p.band0[a]) * rng[a];
+  }
+  if (!fits || off[3] > KTable<D>::CAP) {   // uniform over the block
+    __syncthreads();   // every thread has read the ranges before the caller reuses the LDS
+    return false;
+  }
+  {
+    const int o1 = (int)off[1], o2 = (int)off[2], r0 = (int)rng[0], r1 = (int)rng[1],
+              r2 = (int)rng[2];
+    if (tid < NP) {
+      const int a = (tid >= p.band0[1]) + (tid >= p.band0[2]);
+      const int oa = a == 0 ? 0 : (a == 1 ? o1 : o2);
+      const int ra_ = a == 0 ? r0 : (a == 1 ? r1 : r2);
+      const int ma = a == 0 ? mn[0] : (a == 1 ? mn[1] : mn[2]);
+      const int b0 = a == 0 ? 0 : (a == 1 ? p.band0[1] : p.band0[2]);
+      kt.rb[tid] = oa + (tid - b0) * ra_ - ma;
+    }
+    for (int e = tid; e < (int)off[3]; e += kThreads) {
+      const int a = (e >= o1) + (e >= o2);
+      const int oa = a == 0 ? 0 : (a == 1 ? o1 : o2);
+      const int ra_ = a == 0 ? r0 : (a == 1 ? r1 : r2);
+      const int ma = a == 0 ? mn[0] : (a == 1 ? mn[1] : mn[2]);
+      const int b0 = a == 0 ? 0 : (a == 1 ? p.band0[1] : p.band0[2]);
+      const int within = e - oa;
+      const int pr = b0 + within / ra_;
+      kt.tab[e] = rotary_factors(ma + within % ra_, p.pair_omega[pr]);
+    }
+  }
+  __syncthreads();   // the table visible
+  // vectors of this thread: idx = tid + kThreads * i -> (token ti, vector c);
+  // each pair's table entry is fixed for the tile, every head adds a uniform
+  // offset to the row pointers (h*D in the rows, h*ps*D in the pages)
+  const T* __restrict__ kin = static_cast<const T*>(p.k);
+  T* qio = static_cast<T*>(p.q);
+  T* __restrict__ kpg = static_cast<T*>(p.k_pages);
+  const T* src[PER];
+  T* qptr[PER];
+  T* dst[PER];
+  int ent[PER][EPV / 2];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int idx = tid + kThreads * i;
+    const int ti = idx / VPR, c = idx % VPR;
+    const int L = L0 + ti;
+    const int64_t t = L - p.dst_start;
+    const bool in = L >= lo && L < hi;
+    const int page = in ? page_of[ti] : -1;
+    src[i] = in ? kin + t * p.k_stride + c * EPV : nullptr;
+    qptr[i] = (in && HAS_Q) ? qio + t * p.q_stride + c * EPV : nullptr;
+    dst[i] = page >= 0 ? kpg + ((int64_t)page * p.heads * ps + (L & (ps - 1))) * D + c * EPV
+                       : nullptr;
+    const int4 pz = kt.pos[ti];
+#pragma unroll
+    for (int j = 0; j < EPV / 2; ++j) {
+      const int pr = c * (EPV / 2) + j;
+      const int a = (pr >= p.band0[1]) + (pr >= p.band0[2]);
+      ent[i][j] = kt.rb[pr] + (a == 0 ? pz.x : (a == 1 ? pz.y : pz.z));
+    }
+  }
+  for (int h = h0; h < h1; ++h) {
+    uint4 kv[PER], qv[HAS_Q ? PER : 1];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      if (!src[i]) continue;
+      kv[i] = ld_stream(src[i] + (int64_t)h * D);
+      if constexpr (HAS_Q) qv[i] = *reinterpret_cast<const uint4*>(qptr[i] + (int64_t)h * D);
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      if (!src[i]) continue;
+      float2 cs[EPV / 2];
+#pragma unroll
+      for (int j = 0; j < EPV / 2; ++j) cs[j] = kt.tab[ent[i][j]];
+      rotate_vec<T>(kv[i], cs);
+      if constexpr (HAS_Q) {
+        rotate_vec<T>(qv[i], cs);
+        *reinterpret_cast<uint4*>(qptr[i] + (int64_t)h * D) = qv[i];
+      }
+      if constexpr (MX) {
+        mx_store(p, k8_scales, kv[i], dst[i], h, ps);
+      } else {
+        if (dst[i]) st_device(dst[i] + (int64_t)h * ps * D, kv[i]);
+      }
+    }
+  }
+  return true;
 }
 
 template <int D, bool BF16, bool HAS_Q, bool MX>
@@ -168,8 +333,12 @@ __device__ __forceinline__ void k_block(
   T* __restrict__ kpg = static_cast<T*>(p.k_pages);
 
   tile_pages(p, L0, lo, hi, page_of);
-  // two passes of 32 tokens keep the factor table at half the LDS of the
-  // staged V rows, so K and V blocks reach the same occupancy
+  if (p.rope && k_block_table<D, BF16, HAS_Q, MX>(p, k8_scales, sm.kt, page_of, L0, lo, hi, h0,
+                                                    h1))
+    return;
+  // otherwise (positions spread too widely for the table): factors per
+  // element, in two passes of 32 tokens that keep them at half the LDS of
+  // the staged V rows, so K and V blocks reach the same occupancy
   for (int half = 0; half < 2; ++half) {
     const int T0 = L0 + half * HALF;
     if (half) __syncthreads();   // every thread is done with the previous factors
@@ -353,11 +522,11 @@ __device__ __forceinline__ void v_block_reg(const PublishParams& p, int tile, in
   }
 }
 
-// at least 5 waves per SIMD; the 8-bit variant that also rotates Q needs more
-// registers and takes 4
+// at least 5 waves per SIMD; the variants that also rotate Q need more
+// registers and take 4
 template <int D, bool BF16, bool HAS_Q, bool MX>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
-                          amdgpu_waves_per_eu(MX && HAS_Q ? 4 : 5)))
+                          amdgpu_waves_per_eu(HAS_Q ? 4 : 5)))
 void publish_kernel(const PublishParams p, void* k8_scales) {
   using T = typename std::conditional<BF16, uint16_t, float>::type;
   __shared__ __attribute__((aligned(16))) PublishShared<D, T> sm;

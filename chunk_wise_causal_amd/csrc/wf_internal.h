@@ -32,6 +32,7 @@ struct PublishParams {
   int32_t rope;         // 0/1
   int32_t pair_axis[kMaxPairs];     // axis (0 t, 1 h, 2 w) of each pair
   double pair_omega[kMaxPairs];     // theta^(-2i/d_a) of each pair
+  int32_t band0[4];                 // first pair of the t, h, w sub-bands; band0[3] = D/2
 };
 
 // ---- attention -----------------------------------------------------------
