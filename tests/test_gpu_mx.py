@@ -90,6 +90,40 @@ def case(request):
     return wl, ref, k8, k8s, pool, keys, q
 
 
+def test_publish_mx_positions_beyond_the_factor_table():
+    """As the bfloat16 case: half the tokens on the frame grid (factor table),
+    half with positions spread over +-50000 (per-element factors), one
+    call; the 8-bit key codes, their scales and the V pool bit-exact."""
+    wl = make_workload(medium(page_size=64, seed=54))
+    c = wl.cfg
+    n = c.n_kv
+    rng = np.random.default_rng(c.seed)
+    pos = rng.integers(-50000, 50000, size=(n, 3)).astype(np.int32)
+    pos[: n // 2] = wl.pos[: n // 2]
+    from tests.test_gpu_parity import _factor_table_tiles
+    fit, spill = _factor_table_tiles(pos, c.rope, c.head_dim)
+    assert fit > 0 and spill > 0
+    pool = G.gpu_pool(wl)
+    keys = wf.MXKeys.empty(c.n_pages, c.heads, c.page_size, c.head_dim)
+    keys.codes.fill_(CODE_FILL)
+    keys.scales.fill_(SCALE_FILL)
+    wf.wf_kv_publish_mx(pool, keys, wl.k.to(G.DEV), wl.v.to(G.DEV), 0,
+                        pos=torch.from_numpy(pos).to(G.DEV), rope=(c.rope, c.theta))
+    torch.cuda.synchronize()
+    assert wf.wf_device_status() == 0
+    from oracle.publish import publish
+    from tests._pipeline import empty_pool
+    kp, vp = empty_pool(wl)
+    k_rot, _ = publish(kp, vp, wl.page_table, c.page_size, G.to_storage(wl.k),
+                       G.to_storage(wl.v), pos, 0, c.dtype, rope=(c.rope, c.theta))
+    k8 = np.full((c.n_pages, c.heads, c.page_size, c.head_dim), CODE_FILL, np.uint8)
+    k8s = np.full((c.n_pages, c.heads, c.page_size, c.head_dim // 32), SCALE_FILL, np.uint8)
+    mx_publish_keys(k8, k8s, wl.page_table, c.page_size, k_rot, 0, c.dtype)
+    assert np.array_equal(keys.codes.cpu().numpy(), k8)
+    assert np.array_equal(keys.scales.cpu().numpy(), k8s)
+    assert np.array_equal(G.bits(G.to_storage(pool.v_pages)), G.bits(vp))
+
+
 def test_publish_mx_bit_exact(case):
     wl, ref, k8, k8s, pool, keys, q = case
     assert wf.wf_device_status() == 0

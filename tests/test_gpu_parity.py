@@ -123,6 +123,60 @@ def test_plain_scatter_and_unaligned_window():
     assert np.array_equal(G.bits(G.to_storage(pool.v_pages)), G.bits(vp))
 
 
+def _factor_table_tiles(pos, rope, head_dim, tile=64):
+    """(tiles that fit the K blocks' factor table, tiles that do not): a
+    64-token tile fits when sum over the axes of (pairs of the axis) x
+    (position range of the axis) is at most the table's capacity, the LDS
+    of 32 tokens' per-element factors less the tile's positions, header and
+    row bases, in 8-byte (cos, sin) entries."""
+    pairs = (rope[0] // 2, rope[1] // 2, head_dim // 2 - (rope[0] + rope[1]) // 2)
+    cap = (tile // 2 * (head_dim // 2) * 8 - tile * 16 - 32 - (head_dim // 2) * 4) // 8
+    fit = 0
+    n_tiles = -(-len(pos) // tile)
+    for b in range(n_tiles):
+        p = pos[b * tile:(b + 1) * tile].astype(np.int64)
+        need = sum(pr * (int(p[:, a].max()) - int(p[:, a].min()) + 1) for a, pr in enumerate(pairs))
+        fit += need <= cap
+    return fit, n_tiles - fit
+
+
+@pytest.mark.parametrize(
+    "kw",
+    [dict(page_size=64, seed=51), dict(head_dim=64, rope=(24, 20, 20), page_size=32, seed=52),
+     dict(dtype="fp32", page_size=64, seed=53)],
+    ids=["bf16_d128_ps64", "bf16_d64_ps32", "fp32_d128_ps64"])
+def test_publish_positions_beyond_the_factor_table(kw):
+    """The first half of the tokens keep the frame grid (their K blocks
+    rotate from the per-tile factor table), the second half take positions
+    spread over +-50000 per axis (far more (pair, position) combinations per
+    tile than the table holds: per-element factors).  One call; the pools
+    and the rotated Q bit-exact against the oracle."""
+    wl = make_workload(medium(**kw))
+    c = wl.cfg
+    n = c.n_kv
+    rng = np.random.default_rng(c.seed)
+    pos = rng.integers(-50000, 50000, size=(n, 3)).astype(np.int32)
+    pos[: n // 2] = wl.pos[: n // 2]
+    fit, spill = _factor_table_tiles(pos, c.rope, c.head_dim)
+    assert fit > 0 and spill > 0
+    g = torch.Generator().manual_seed(c.seed)
+    q = torch.randn(n, c.heads, c.head_dim, generator=g).to(wl.torch_dtype)
+    pool = G.gpu_pool(wl)
+    q_io = q.to(G.DEV).clone()
+    wf.wf_kv_publish(pool, wl.k.to(G.DEV), wl.v.to(G.DEV), 0, pos=torch.from_numpy(pos).to(G.DEV),
+                     rope=(c.rope, c.theta), q=q_io)
+    torch.cuda.synchronize()
+    assert wf.wf_device_status() == 0
+    from oracle.publish import publish
+    from tests._pipeline import empty_pool
+    kp, vp = empty_pool(wl)
+    _, q_rot = publish(kp, vp, wl.page_table, c.page_size, G.to_storage(wl.k), G.to_storage(wl.v),
+                       pos, 0, c.dtype, rope=(c.rope, c.theta), q=G.to_storage(q))
+    assert np.array_equal(G.bits(G.to_storage(pool.k_pages)), G.bits(kp))
+    assert np.array_equal(G.bits(G.to_storage(pool.v_pages)), G.bits(vp))
+    assert np.array_equal(G.bits(G.to_storage(q_io)), G.bits(q_rot))
+
+
 @pytest.mark.parametrize("cols", [13, 12], ids=["chunk390", "chunk360_packed"])
 def test_first_slot_share_equals_full_call(cols):
     """One slot per call equals that slot's rows of the full call, bit for
