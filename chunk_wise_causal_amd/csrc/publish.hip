@@ -466,10 +466,11 @@ __device__ __forceinline__ void v_block(
 // or 4 of 64).  Wave w takes a 64-feature block of one head; lane (c, g)
 // loads the 16-byte vectors c (features 8c..8c+7 of the block) of tokens
 // 8g..8g+7, transposes the 8 x 8 block in registers and stores 8 runs of 8
-// consecutive tokens, one per feature, into the d-major V page.
+// consecutive tokens, one per feature, into the d-major V page.  An aligned
+// run of 8 tokens lies in one page (pages hold at least 16), so each lane
+// reads its own page entry: no shared page list and no barrier.
 template <int D>
-__device__ __forceinline__ void v_block_reg(const PublishParams& p, int tile, int vb,
-                                            int* page_of) {
+__device__ __forceinline__ void v_block_reg(const PublishParams& p, int tile, int vb) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int fb = vb * (kThreads / 64) + wave;          // 64-feature block
   const int h = fb / (D / 64), f0 = (fb % (D / 64)) * 64;
@@ -490,14 +491,13 @@ __device__ __forceinline__ void v_block_reg(const PublishParams& p, int tile, in
     if (live && L >= lo && L < hi)
       r[j] = ld_stream(vin + (int64_t)(L - p.dst_start) * p.v_stride + (int64_t)h * D + f0 + 8 * c);
   }
-  tile_pages(p, L0, lo, hi, page_of);
-  __syncthreads();
   if (!live || Lg + 8 <= lo || Lg >= hi) return;
-  int page = -1;
-#pragma unroll
-  for (int e = 0; e < 8; ++e)
-    if (Lg + e >= lo && Lg + e < hi) page = page_of[8 * g + e];
-  if (page < 0) return;
+  // host validation keeps L >> ps_log2 < num_logical_pages for published rows
+  const int page = p.page_table[max(Lg, lo) >> p.ps_log2];
+  if (page < 0 || page >= p.num_pages) {
+    atomicOr(p.status, WF_STATUS_BAD_PAGE);
+    return;
+  }
   uint16_t* dst = vpg + (((int64_t)page * p.heads + h) * D + f0 + 8 * c) * ps + (Lg & (ps - 1));
   const bool full = Lg >= lo && Lg + 8 <= hi;
 #pragma unroll
@@ -536,7 +536,7 @@ void publish_kernel(const PublishParams p, void* k8_scales) {
     k_block<D, BF16, HAS_Q, MX>(p, k8_scales, b, sm, page_of);
   } else {
     const int vb = b - p.k_blocks;
-    if constexpr (BF16) v_block_reg<D>(p, vb % p.tiles, vb / p.tiles, page_of);
+    if constexpr (BF16) v_block_reg<D>(p, vb % p.tiles, vb / p.tiles);
     else v_block<D, BF16>(p, vb, sm, page_of);
   }
 }
