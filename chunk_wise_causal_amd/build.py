@@ -26,6 +26,12 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          "-Wall", "-Wno-unused-command-line-argument", f"-I{INCLUDE}"]
 
 
+# per-source options: the 8-bit attention kernel's grouping hints name only the
+# vector work and the reads and leave its block-scaled products to the machine
+# scheduler, which places them better with the maximum-ILP strategy
+SOURCE_FLAGS = {"attn_mx.hip": ["-mllvm", "--amdgpu-sched-strategy=max-ilp"]}
+
+
 def hipcc() -> str:
     rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
     path = os.path.join(rocm, "bin", "hipcc")
@@ -41,7 +47,8 @@ def build(verbose: bool = False, jobs: int = 0) -> str:
     def compile_one(src):
         obj = os.path.join(build_dir, src + ".o")
         lang = ["-x", "hip"] if src.endswith(".cpp") else []
-        _run([hipcc(), *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
+        _run([hipcc(), *FLAGS, *SOURCE_FLAGS.get(src, []), *lang, "-c", os.path.join(CSRC, src),
+              "-o", obj], verbose)
         return obj
 
     workers = jobs or max(1, min(8, os.cpu_count() or 1))
